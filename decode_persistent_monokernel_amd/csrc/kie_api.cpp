@@ -1,0 +1,533 @@
+// Host side of the C ABI declared in include/kie.h: argument validation,
+// buffer sizing, the weight packer, workspace set-up and the launches of the
+// persistent decode kernel.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "kie.h"
+#include "kie_layout.h"
+
+extern "C" hipError_t kie_internal_launch(const kie::KParams* kp, int nwg, size_t lds_bytes, hipStream_t stream);
+extern "C" hipError_t kie_internal_zero(void* p, size_t bytes, hipStream_t stream);
+extern "C" hipError_t kie_internal_occupancy(int G, size_t lds_bytes, int* blocks_per_cu);
+
+struct kie_ctx {
+  kie_model_config cfg;
+  kie::Dims m;
+  int device = -1;
+  int nwg = 256;
+  kie::PackLayout pl;
+  kie::WsLayout wl;
+  kie::LdsPlan lp;
+  void* packed = nullptr;
+  void* kv = nullptr;
+  void* ws = nullptr;
+  bool bound = false;
+  bool loaded = false;
+  int32_t pos = 0;
+  uint32_t next_epoch = 1;  // epoch of the next decode step (0 = never written)
+  uint64_t timeout_us = 2000000;
+  uint32_t debug = 0;
+  int32_t launch_steps = 512;
+  double clock_khz = 100000.0;
+  std::string err;
+};
+
+namespace {
+
+kie_status fail(kie_ctx* c, kie_status s, const std::string& msg) {
+  if (c) c->err = msg;
+  return s;
+}
+
+kie_status hip_fail(kie_ctx* c, hipError_t e, const char* what) {
+  return fail(c, KIE_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+std::string check_config(const kie_model_config& c) {
+  if (c.n_layers <= 0 || c.d_model <= 0 || c.n_heads <= 0 || c.n_kv_heads <= 0 || c.head_dim <= 0 ||
+      c.ffn_dim <= 0 || c.vocab <= 0 || c.max_ctx <= 0)
+    return "all sizes must be positive";
+  if (c.n_heads % c.n_kv_heads) return "n_heads must be a multiple of n_kv_heads";
+  if (c.head_dim % 8) return "head_dim must be a multiple of 8";
+  if (c.d_model % 8 || (c.n_heads * c.head_dim) % 8 || c.ffn_dim % 8)
+    return "d_model, n_heads*head_dim and ffn_dim must be multiples of 8";
+  if (c.n_lanes <= 0 || c.n_heads % c.n_lanes || c.ffn_dim % c.n_lanes)
+    return "n_lanes must divide n_heads and ffn_dim";
+  if (c.parallel_block != 0 && c.parallel_block != 1) return "parallel_block must be 0 or 1";
+  if (c.lane_delay < 0) return "lane_delay must be >= 0";
+  if (!c.parallel_block && c.lane_delay) return "lane_delay needs parallel_block = 1";
+  if (!(c.rms_eps >= 0.f) || !(c.rope_base > 1.0)) return "rms_eps must be >= 0 and rope_base > 1";
+  return "";
+}
+
+kie::Dims make_dims(const kie_model_config& c) {
+  kie::Dims m{};
+  m.L = c.n_layers;
+  m.d = c.d_model;
+  m.H = c.n_heads;
+  m.Hkv = c.n_kv_heads;
+  m.hd = c.head_dim;
+  m.F = c.ffn_dim;
+  m.V = c.vocab;
+  m.G = c.n_heads / c.n_kv_heads;
+  m.max_ctx = c.max_ctx;
+  m.parallel = c.parallel_block;
+  m.delay = c.lane_delay;
+  m.eps = c.rms_eps;
+  return m;
+}
+
+std::string check_supported(const kie::Dims& m, int nwg) {
+  if (m.G != 1 && m.G != 2 && m.G != 4) return "query heads per KV head must be 1, 2 or 4";
+  if (m.hd / 8 > 64) return "head_dim above 512 is not supported";
+  if (m.Hkv > nwg) return "more KV heads than workgroups";
+  const kie::LdsPlan lp = kie::lds_plan(m, nwg);
+  if (lp.total_floats > kie::kMainFloats) return "model needs more LDS than the kernel reserves";
+  const uint64_t lim = 0x7FFFFFFFull;
+  if ((uint64_t)m.Hkv * (uint64_t)(m.max_ctx + 1) * (uint64_t)nwg > lim) return "KV heads x context too large";
+  if ((uint64_t)m.V * (uint64_t)nwg > lim || (uint64_t)2 * m.F * (uint64_t)nwg > lim)
+    return "vocab or ffn too large for the partition arithmetic";
+  if ((uint64_t)m.V * (uint64_t)m.d >= (1ull << 32)) return "LM head too large";
+  return "";
+}
+
+// ---------------------------------------------------------------------------
+// packer
+// ---------------------------------------------------------------------------
+void copy_rows(uint16_t* dst, const uint16_t* src, size_t n) { std::memcpy(dst, src, n * sizeof(uint16_t)); }
+
+bool weights_complete(const kie_model_config& c, const kie_weights* w) {
+  if (!w || !w->embed || !w->lm_head || !w->final_norm || !w->attn_norm || !w->wq || !w->wk || !w->wv || !w->wo ||
+      !w->mlp_norm || !w->w_gate || !w->w_up || !w->w_down)
+    return false;
+  for (int l = 0; l < c.n_layers; ++l)
+    if (!w->attn_norm[l] || !w->wq[l] || !w->wk[l] || !w->wv[l] || !w->wo[l] || !w->mlp_norm[l] || !w->w_gate[l] ||
+        !w->w_up[l] || !w->w_down[l])
+      return false;
+  return true;
+}
+
+// pack layer l into dst (layer_stride elements)
+void pack_layer(const kie::Dims& m, const kie::PackLayout& pl, const kie_weights* w, int l, uint16_t* dst) {
+  const size_t d = m.d, qd = (size_t)m.H * m.hd, F = m.F;
+  std::memset(dst, 0, pl.layer_stride * sizeof(uint16_t));
+  copy_rows(dst + pl.attn_norm, w->attn_norm[l], d);
+  const int rows = (m.H + 2 * m.Hkv) * m.hd;
+  for (int r = 0; r < rows; ++r) {
+    int which, src;
+    kie::qkv_source_row(m, r, &which, &src);
+    const uint16_t* s = which == 0 ? w->wq[l] : which == 1 ? w->wk[l] : w->wv[l];
+    copy_rows(dst + pl.wqkv + (size_t)r * d, s + (size_t)src * d, d);
+  }
+  copy_rows(dst + pl.wo, w->wo[l], d * qd);
+  copy_rows(dst + pl.mlp_norm, w->mlp_norm[l], d);
+  for (size_t f = 0; f < F; ++f) {
+    copy_rows(dst + pl.wgu + (2 * f) * d, w->w_gate[l] + f * d, d);
+    copy_rows(dst + pl.wgu + (2 * f + 1) * d, w->w_up[l] + f * d, d);
+  }
+  copy_rows(dst + pl.wd, w->w_down[l], d * F);
+}
+
+// the part after the layers: final_norm, lm_head, embed
+void pack_tail(const kie::Dims& m, const kie::PackLayout& pl, const kie_weights* w, uint16_t* dst_at_final_norm) {
+  const uint64_t base = pl.final_norm;
+  std::memset(dst_at_final_norm, 0, (pl.total - base) * sizeof(uint16_t));
+  copy_rows(dst_at_final_norm + (pl.final_norm - base), w->final_norm, m.d);
+  copy_rows(dst_at_final_norm + (pl.lm_head - base), w->lm_head, (size_t)m.V * m.d);
+  copy_rows(dst_at_final_norm + (pl.embed - base), w->embed, (size_t)m.V * m.d);
+}
+
+// RoPE table: (cos, sin) of pos * base^(-2i/hd), computed in double
+void rope_table(const kie::Dims& m, double base, std::vector<float>& out) {
+  const int half = m.hd / 2;
+  out.resize((size_t)m.max_ctx * half * 2);
+  std::vector<double> inv(half);
+  for (int i = 0; i < half; ++i) inv[i] = std::pow(base, -2.0 * i / m.hd);
+  for (int p = 0; p < m.max_ctx; ++p)
+    for (int i = 0; i < half; ++i) {
+      const double a = (double)p * inv[i];
+      out[((size_t)p * half + i) * 2] = (float)std::cos(a);
+      out[((size_t)p * half + i) * 2 + 1] = (float)std::sin(a);
+    }
+}
+
+kie::KParams base_params(const kie_ctx* c) {
+  kie::KParams kp{};
+  kp.m = c->m;
+  kp.pl = c->pl;
+  kp.wl = c->wl;
+  kp.lp = c->lp;
+  kp.W = (const uint16_t*)c->packed;
+  kp.kv = (uint16_t*)c->kv;
+  kp.ws = (uint8_t*)c->ws;
+  kp.timeout_ticks = (uint64_t)((double)c->timeout_us * c->clock_khz / 1000.0);
+  if (kp.timeout_ticks == 0) kp.timeout_ticks = 1;
+  kp.debug_flags = c->debug;
+  return kp;
+}
+
+kie_status ready(kie_ctx* c) {
+  if (!c) return KIE_ERR_INVALID_ARG;
+  if (c->device < 0) return fail(c, KIE_ERR_STATE, "host-only context");
+  if (!c->bound) return fail(c, KIE_ERR_STATE, "memory not bound");
+  if (!c->loaded) return fail(c, KIE_ERR_STATE, "weights not loaded");
+  return KIE_OK;
+}
+
+kie_status launch(kie_ctx* c, kie::KParams& kp, hipStream_t st) {
+  hipError_t e = hipSetDevice(c->device);
+  if (e != hipSuccess) return hip_fail(c, e, "hipSetDevice");
+  e = kie_internal_launch(&kp, c->nwg, 0, st);
+  if (e != hipSuccess) return hip_fail(c, e, "monokernel launch");
+  c->next_epoch += (uint32_t)kp.n_steps;
+  return KIE_OK;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// C ABI
+// ---------------------------------------------------------------------------
+extern "C" {
+
+kie_status kie_create(const kie_model_config* cfg, int device, kie_ctx** out) {
+  if (!cfg || !out) return KIE_ERR_INVALID_ARG;
+  *out = nullptr;
+  const std::string msg = check_config(*cfg);
+  if (!msg.empty()) {
+    std::fprintf(stderr, "kie_create: %s\n", msg.c_str());
+    return KIE_ERR_INVALID_ARG;
+  }
+  kie_ctx* c = new kie_ctx();
+  c->cfg = *cfg;
+  c->m = make_dims(*cfg);
+  c->device = device;
+  if (device >= 0) {
+    hipError_t e = hipSetDevice(device);
+    hipDeviceProp_t prop;
+    if (e == hipSuccess) e = hipGetDeviceProperties(&prop, device);
+    if (e != hipSuccess) {
+      std::fprintf(stderr, "kie_create: %s\n", hipGetErrorString(e));
+      delete c;
+      return KIE_ERR_HIP;
+    }
+    c->nwg = prop.multiProcessorCount;
+    int khz = 0;
+    if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, device) == hipSuccess && khz > 0)
+      c->clock_khz = khz;
+  }
+  const std::string sup = check_supported(c->m, c->nwg);
+  if (!sup.empty()) {
+    std::fprintf(stderr, "kie_create: %s\n", sup.c_str());
+    delete c;
+    return KIE_ERR_UNSUPPORTED;
+  }
+  if (device >= 0) {
+    int per_cu = 0;
+    hipError_t e = kie_internal_occupancy(c->m.G, 0, &per_cu);
+    if (e != hipSuccess || per_cu < 1) {
+      std::fprintf(stderr, "kie_create: kernel does not fit a compute unit (%s)\n",
+                   e == hipSuccess ? "occupancy 0" : hipGetErrorString(e));
+      delete c;
+      return KIE_ERR_UNSUPPORTED;
+    }
+  }
+  c->pl = kie::pack_layout(c->m);
+  c->wl = kie::ws_layout(c->m, c->nwg);
+  c->lp = kie::lds_plan(c->m, c->nwg);
+  *out = c;
+  return KIE_OK;
+}
+
+kie_status kie_query_sizes(const kie_ctx* c, size_t* packed, size_t* kv, size_t* ws) {
+  if (!c) return KIE_ERR_INVALID_ARG;
+  if (packed) *packed = (size_t)c->pl.total * 2;
+  if (kv) *kv = (size_t)kie::kv_elems(c->m) * 2;
+  if (ws) *ws = (size_t)c->wl.total;
+  return KIE_OK;
+}
+
+kie_status kie_bind_memory(kie_ctx* c, void* d_packed, void* d_kv, void* d_ws) {
+  if (!c) return KIE_ERR_INVALID_ARG;
+  if (c->device < 0) return fail(c, KIE_ERR_STATE, "host-only context");
+  if (!d_packed || !d_kv || !d_ws) return fail(c, KIE_ERR_INVALID_ARG, "null device pointer");
+  if (((uintptr_t)d_packed | (uintptr_t)d_kv | (uintptr_t)d_ws) & 255)
+    return fail(c, KIE_ERR_INVALID_ARG, "device buffers must be 256-byte aligned");
+  hipError_t e = hipSetDevice(c->device);
+  if (e != hipSuccess) return hip_fail(c, e, "hipSetDevice");
+  c->packed = d_packed;
+  c->kv = d_kv;
+  c->ws = d_ws;
+  c->bound = true;
+  c->loaded = false;
+  c->pos = 0;
+  c->next_epoch = 1;
+  // clear state and exchange words, upload the RoPE table
+  uint8_t* w = (uint8_t*)d_ws;
+  if ((e = kie_internal_zero(w + c->wl.state, 256, nullptr)) != hipSuccess) return hip_fail(c, e, "clear state");
+  if ((e = kie_internal_zero(w + c->wl.ll_begin, c->wl.ll_end - c->wl.ll_begin, nullptr)) != hipSuccess)
+    return hip_fail(c, e, "clear exchange words");
+  std::vector<float> rope;
+  rope_table(c->m, c->cfg.rope_base, rope);
+  if ((e = hipMemcpy(w + c->wl.rope, rope.data(), rope.size() * sizeof(float), hipMemcpyHostToDevice)) != hipSuccess)
+    return hip_fail(c, e, "upload RoPE table");
+  if ((e = hipDeviceSynchronize()) != hipSuccess) return hip_fail(c, e, "bind");
+  return KIE_OK;
+}
+
+kie_status kie_load_weights(kie_ctx* c, const kie_weights* src, void* stream) {
+  if (!c) return KIE_ERR_INVALID_ARG;
+  if (c->device < 0) return fail(c, KIE_ERR_STATE, "host-only context");
+  if (!c->bound) return fail(c, KIE_ERR_STATE, "memory not bound");
+  if (!weights_complete(c->cfg, src)) return fail(c, KIE_ERR_INVALID_ARG, "missing weight pointer");
+  hipError_t e = hipSetDevice(c->device);
+  if (e != hipSuccess) return hip_fail(c, e, "hipSetDevice");
+  hipStream_t st = (hipStream_t)stream;
+  if ((e = hipStreamSynchronize(st)) != hipSuccess) return hip_fail(c, e, "stream sync");
+  std::vector<uint16_t> buf(c->pl.layer_stride);
+  uint16_t* dst = (uint16_t*)c->packed;
+  for (int l = 0; l < c->m.L; ++l) {
+    pack_layer(c->m, c->pl, src, l, buf.data());
+    e = hipMemcpy(dst + (size_t)l * c->pl.layer_stride, buf.data(), buf.size() * 2, hipMemcpyHostToDevice);
+    if (e != hipSuccess) return hip_fail(c, e, "upload layer");
+  }
+  std::vector<uint16_t> tail(c->pl.total - c->pl.final_norm);
+  pack_tail(c->m, c->pl, src, tail.data());
+  e = hipMemcpy(dst + c->pl.final_norm, tail.data(), tail.size() * 2, hipMemcpyHostToDevice);
+  if (e != hipSuccess) return hip_fail(c, e, "upload head");
+  c->loaded = true;
+  return KIE_OK;
+}
+
+kie_status kie_prefill(kie_ctx* c, const int32_t* d_prompt, int32_t n, int32_t* d_next, float* d_logits,
+                       void* stream) {
+  kie_status s = ready(c);
+  if (s != KIE_OK) return s;
+  if (!d_prompt || n <= 0) return fail(c, KIE_ERR_INVALID_ARG, "empty prompt");
+  if ((int64_t)c->pos + n > c->m.max_ctx) return fail(c, KIE_ERR_CAPACITY, "prompt exceeds max_ctx");
+  hipStream_t st = (hipStream_t)stream;
+  for (int32_t off = 0; off < n;) {
+    const int32_t chunk = std::min<int32_t>(c->launch_steps, n - off);
+    const bool last = off + chunk == n;
+    kie::KParams kp = base_params(c);
+    kp.forced = d_prompt + off;
+    kp.out = last ? d_next : nullptr;
+    kp.logits = last ? d_logits : nullptr;
+    kp.n_steps = chunk;
+    kp.pos0 = c->pos;
+    kp.lm_mode = last ? 1 : 2;
+    kp.first_from_state = 0;
+    kp.epoch0 = c->next_epoch;
+    if ((s = launch(c, kp, st)) != KIE_OK) return s;
+    c->pos += chunk;
+    off += chunk;
+  }
+  return KIE_OK;
+}
+
+kie_status kie_decode(kie_ctx* c, int32_t n, int32_t* d_out, const int32_t* d_forced, float* d_logits,
+                      void* stream) {
+  kie_status s = ready(c);
+  if (s != KIE_OK) return s;
+  if (n <= 0) return fail(c, KIE_ERR_INVALID_ARG, "n_tokens must be >= 1");
+  if ((int64_t)c->pos + n > c->m.max_ctx) return fail(c, KIE_ERR_CAPACITY, "decode exceeds max_ctx");
+  hipStream_t st = (hipStream_t)stream;
+  for (int32_t off = 0; off < n;) {
+    const int32_t chunk = std::min<int32_t>(c->launch_steps, n - off);
+    kie::KParams kp = base_params(c);
+    kp.forced = d_forced ? d_forced + off : nullptr;
+    kp.out = d_out ? d_out + off : nullptr;
+    kp.logits = d_logits ? d_logits + (size_t)off * c->m.V : nullptr;
+    kp.n_steps = chunk;
+    kp.pos0 = c->pos;
+    kp.lm_mode = 0;
+    kp.first_from_state = 1;
+    kp.epoch0 = c->next_epoch;
+    if ((s = launch(c, kp, st)) != KIE_OK) return s;
+    c->pos += chunk;
+    off += chunk;
+  }
+  return KIE_OK;
+}
+
+kie_status kie_set_position(kie_ctx* c, int32_t pos, int32_t next_token, void* stream) {
+  if (!c) return KIE_ERR_INVALID_ARG;
+  if (pos < 0 || pos > c->m.max_ctx) return fail(c, KIE_ERR_INVALID_ARG, "position out of range");
+  if (next_token < 0 || next_token >= c->m.V) return fail(c, KIE_ERR_INVALID_ARG, "token out of range");
+  if (c->device < 0 || !c->bound) return fail(c, KIE_ERR_STATE, "memory not bound");
+  hipError_t e = hipSetDevice(c->device);
+  if (e == hipSuccess)
+    e = hipMemsetD32Async((hipDeviceptr_t)((uint8_t*)c->ws + c->wl.state + 8), next_token, 1, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(c, e, "set token");
+  c->pos = pos;
+  return KIE_OK;
+}
+
+kie_status kie_sync_status(kie_ctx* c, void* stream) {
+  if (!c) return KIE_ERR_INVALID_ARG;
+  if (c->device < 0 || !c->bound) return fail(c, KIE_ERR_STATE, "memory not bound");
+  hipError_t e = hipSetDevice(c->device);
+  if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(c, e, "stream sync");
+  int32_t st[2] = {0, 0};
+  e = hipMemcpy(st, (uint8_t*)c->ws + c->wl.state, sizeof(st), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(c, e, "read status");
+  if (st[0] == 0 && st[1] == 0) return KIE_OK;
+  const int32_t zero[2] = {0, 0};
+  e = hipMemcpy((uint8_t*)c->ws + c->wl.state, zero, sizeof(zero), hipMemcpyHostToDevice);
+  if (e != hipSuccess) return hip_fail(c, e, "clear status");
+  if (st[0] == kie::DEV_BAD_TOKEN) return fail(c, KIE_ERR_BAD_TOKEN, "a token id outside [0, vocab) reached the kernel");
+  return fail(c, KIE_ERR_TIMEOUT, "a wait inside the decode kernel timed out");
+}
+
+kie_status kie_set_timeout_us(kie_ctx* c, uint64_t us) {
+  if (!c || us == 0) return KIE_ERR_INVALID_ARG;
+  c->timeout_us = us;
+  return KIE_OK;
+}
+
+kie_status kie_set_debug_flags(kie_ctx* c, uint32_t flags) {
+  if (!c) return KIE_ERR_INVALID_ARG;
+  c->debug = flags;
+  return KIE_OK;
+}
+
+kie_status kie_set_launch_steps(kie_ctx* c, int32_t steps) {
+  if (!c || steps <= 0) return KIE_ERR_INVALID_ARG;
+  c->launch_steps = steps;
+  return KIE_OK;
+}
+
+kie_status kie_pack_weights_host(const kie_model_config* cfg, const kie_weights* src, void* host_dst) {
+  if (!cfg || !host_dst) return KIE_ERR_INVALID_ARG;
+  if (!check_config(*cfg).empty()) return KIE_ERR_INVALID_ARG;
+  if (!weights_complete(*cfg, src)) return KIE_ERR_INVALID_ARG;
+  const kie::Dims m = make_dims(*cfg);
+  const kie::PackLayout pl = kie::pack_layout(m);
+  uint16_t* dst = (uint16_t*)host_dst;
+  for (int l = 0; l < m.L; ++l) pack_layer(m, pl, src, l, dst + (size_t)l * pl.layer_stride);
+  pack_tail(m, pl, src, dst + pl.final_norm);
+  return KIE_OK;
+}
+
+kie_status kie_launch_info(const kie_ctx* c, int32_t* nwg, int32_t* threads, int32_t* lds, int64_t* qkv_off,
+                           int64_t* lm_off) {
+  if (!c) return KIE_ERR_INVALID_ARG;
+  if (nwg) *nwg = c->nwg;
+  if (threads) *threads = kie::kThreads;
+  if (lds) *lds = kie::kMainFloats * 4 + kie::kWaves * kie::kRingDepth * 1024;
+  if (qkv_off) *qkv_off = (int64_t)c->pl.wqkv;
+  if (lm_off) *lm_off = (int64_t)c->pl.lm_head;
+  return KIE_OK;
+}
+
+kie_status kie_validate_schedule(const kie_model_config* cfg, int32_t nwg, int32_t n_ctx, char* msg, size_t msg_len) {
+  auto bad = [&](const std::string& s) {
+    if (msg && msg_len) std::snprintf(msg, msg_len, "%s", s.c_str());
+    return KIE_ERR_INVALID_ARG;
+  };
+  if (!cfg || nwg <= 0 || n_ctx <= 0) return bad("bad arguments");
+  const std::string cm = check_config(*cfg);
+  if (!cm.empty()) return bad(cm);
+  const kie::Dims m = make_dims(*cfg);
+  const std::string sup = check_supported(m, nwg);
+  if (!sup.empty()) return bad(sup);
+  // GEMV: rows and (row, block) units
+  const int kinds[5] = {kie::PH_QKV, kie::PH_O, kie::PH_GU, kie::PH_DOWN, kie::PH_LM};
+  for (int k : kinds) {
+    const kie::GemvShape sh = kie::gemv_shape(m, k);
+    std::vector<int> owner(sh.rows, -1);
+    for (int w = 0; w < nwg; ++w) {
+      int r0, r1;
+      kie::gemv_rows(m, k, nwg, w, &r0, &r1);
+      if (r0 % sh.unit_rows || r1 % sh.unit_rows) return bad("row range splits a row group");
+      for (int r = r0; r < r1; ++r) {
+        if (r < 0 || r >= sh.rows || owner[r] != -1) return bad("GEMV row owned twice or out of range");
+        owner[r] = w;
+      }
+      const int nb = kie::blocks_per_row(sh.K);
+      std::vector<int> seen((size_t)(r1 - r0) * nb, 0);
+      int prev_end = 0;
+      for (int wave = 0; wave < kie::kWaves; ++wave) {
+        int u0, u1;
+        kie::gemv_wave_units(r1 - r0, sh.K, wave, &u0, &u1);
+        if (u0 != prev_end || u1 < u0) return bad("wave unit ranges not contiguous");
+        prev_end = u1;
+        for (int u = u0; u < u1; ++u) seen[u]++;
+      }
+      if (prev_end != (r1 - r0) * nb) return bad("wave units do not cover the workgroup rows");
+      for (int v : seen)
+        if (v != 1) return bad("GEMV unit covered twice");
+    }
+    for (int r = 0; r < sh.rows; ++r)
+      if (owner[r] < 0) return bad("GEMV row not owned");
+  }
+  // attention: keys, segments, mergers
+  const int kpl = kie::attn_kpl(m.hd);
+  std::vector<int> key_owner((size_t)m.Hkv * n_ctx, 0);
+  std::vector<int> mergers(m.Hkv, 0);
+  const int pos = n_ctx - 1;
+  for (int w = 0; w < nwg; ++w) {
+    kie::AttnSeg seg[2];
+    const int ns = kie::attn_segments(m.Hkv, n_ctx, nwg, w, seg);
+    int fa, fb;
+    kie::split(m.Hkv * n_ctx, nwg, w, &fa, &fb);
+    int covered = 0;
+    for (int s = 0; s < ns; ++s) {
+      covered += seg[s].tb - seg[s].ta;
+      if (seg[s].tb == n_ctx) mergers[seg[s].g]++;
+      for (int wave = 0; wave < kie::kWaves; ++wave) {
+        int wa, wb;
+        kie::split(seg[s].tb - seg[s].ta, kie::kWaves, wave, &wa, &wb);
+        wa += seg[s].ta;
+        wb += seg[s].ta;
+        for (int t = wa; t < wb; ++t) key_owner[(size_t)seg[s].g * n_ctx + t]++;
+        const int kc = std::max(wa, std::min(wb, pos));
+        const int nst = (kc - wa + kpl - 1) / kpl;
+        if (nst * kpl < kc - wa) return bad("attention steps miss keys");
+      }
+      if (kie::attn_owner(m.Hkv, n_ctx, nwg, seg[s].g, seg[s].ta) != w)
+        return bad("attn_owner disagrees with attn_segments");
+    }
+    if (covered != fb - fa) return bad("workgroup range meets more than two heads");
+  }
+  for (int v : key_owner)
+    if (v != 1) return bad("attention key covered zero or several times");
+  const kie::LdsPlan lp = kie::lds_plan(m, nwg);
+  for (int g = 0; g < m.Hkv; ++g) {
+    const int nrec = kie::attn_owner(m.Hkv, n_ctx, nwg, g, n_ctx - 1) - kie::attn_owner(m.Hkv, n_ctx, nwg, g, 0) + 1;
+    if (nrec > lp.max_recs) return bad("more attention records per head than the LDS plan holds");
+  }
+  for (int v : mergers)
+    if (v != 1) return bad("a KV head has no merger or several");
+  return KIE_OK;
+}
+
+int32_t kie_position(const kie_ctx* c) { return c ? c->pos : -1; }
+
+const char* kie_status_string(kie_status s) {
+  switch (s) {
+    case KIE_OK: return "ok";
+    case KIE_ERR_INVALID_ARG: return "invalid argument";
+    case KIE_ERR_HIP: return "HIP runtime error";
+    case KIE_ERR_CAPACITY: return "KV-cache capacity exceeded";
+    case KIE_ERR_STATE: return "context not ready";
+    case KIE_ERR_TIMEOUT: return "wait timed out inside the kernel";
+    case KIE_ERR_UNSUPPORTED: return "unsupported model shape";
+    case KIE_ERR_BAD_TOKEN: return "token id out of range";
+  }
+  return "unknown status";
+}
+
+const char* kie_last_error(const kie_ctx* c) { return c ? c->err.c_str() : "null context"; }
+
+void kie_destroy(kie_ctx* c) { delete c; }
+
+}  // extern "C"

@@ -1,0 +1,305 @@
+// Layouts and work partitions shared by the host library and the monokernel.
+//
+// Everything here is plain integer arithmetic: where each packed weight
+// matrix lives, where each workspace buffer lives, and which rows / keys each
+// workgroup and wave owns.  The host uses the same functions to size buffers
+// and to validate a schedule on the CPU; the device uses them to find its work.
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__HIPCC__)
+#define KIE_HD __host__ __device__ __forceinline__
+#else
+#define KIE_HD static inline
+#endif
+
+namespace kie {
+
+constexpr int kWave = 64;               // lanes per wavefront (CDNA)
+constexpr int kWaves = 8;               // wavefronts per workgroup
+constexpr int kThreads = kWave * kWaves;
+constexpr int kBlock = 512;             // fp16 elements one wave reads with 16 B per lane
+constexpr int kBlock8 = kBlock / 8;     // 16-byte segments per block (= lanes)
+
+enum PhaseKind : int { PH_QKV = 0, PH_ATTN = 1, PH_O = 2, PH_GU = 3, PH_DOWN = 4, PH_LM = 5 };
+
+// phase order inside one layer
+//   sequential pre-norm block: QKV ATTN O GU DOWN
+//   parallel (lane) block:     QKV GU ATTN O DOWN   (attention and MLP both read x_l)
+KIE_HD int phase_kind(int parallel, int j) {
+  return parallel ? (j == 0 ? PH_QKV : j == 1 ? PH_GU : j == 2 ? PH_ATTN : j == 3 ? PH_O : PH_DOWN)
+                  : j;  // enum order is the sequential order
+}
+
+struct Dims {
+  int L, d, H, Hkv, hd, F, V, G, max_ctx;
+  int parallel, delay;
+  float eps;
+};
+
+// ---------------------------------------------------------------------------
+// packed weights (offsets in fp16 elements from the packed base)
+//
+// Per layer, in order: attn_norm[d], Wqkv[(H+2Hkv)hd][d], Wo[d][H hd],
+// mlp_norm[d], Wgu[2F][d], Wd[d][F]; then final_norm[d], Wlm[V][d], E[V][d].
+// Matrices stay row-major [out][in] (a row is the contiguous K-vector one
+// output consumes) with two row permutations:
+//   * Wqkv: inside every q and k head, packed row 2i is dim i and row 2i+1 is
+//     dim i + hd/2, so the rotate-half RoPE pair of an output sits in one
+//     workgroup; v rows are in natural order;
+//   * Wgu: packed row 2f is gate row f, row 2f+1 is up row f.
+// Each tensor starts on a 256-byte boundary.
+// ---------------------------------------------------------------------------
+struct PackLayout {
+  uint64_t layer_stride;
+  uint64_t attn_norm, wqkv, wo, mlp_norm, wgu, wd;  // within a layer
+  uint64_t final_norm, lm_head, embed;              // absolute
+  uint64_t total;                                   // elements
+};
+
+KIE_HD uint64_t align_up(uint64_t x, uint64_t a) { return (x + a - 1) / a * a; }
+
+KIE_HD PackLayout pack_layout(const Dims& m) {
+  const uint64_t A = 128;  // 256 bytes
+  PackLayout p{};
+  uint64_t o = 0;
+  const uint64_t d = m.d, qd = (uint64_t)m.H * m.hd, kvd = (uint64_t)m.Hkv * m.hd, F = m.F;
+  p.attn_norm = o; o = align_up(o + d, A);
+  p.wqkv = o; o = align_up(o + (qd + 2 * kvd) * d, A);
+  p.wo = o; o = align_up(o + d * qd, A);
+  p.mlp_norm = o; o = align_up(o + d, A);
+  p.wgu = o; o = align_up(o + 2 * F * d, A);
+  p.wd = o; o = align_up(o + d * F, A);
+  p.layer_stride = o;
+  o = p.layer_stride * (uint64_t)m.L;
+  p.final_norm = o; o = align_up(o + d, A);
+  p.lm_head = o; o = align_up(o + (uint64_t)m.V * d, A);
+  p.embed = o; o = align_up(o + (uint64_t)m.V * d, A);
+  p.total = o;
+  return p;
+}
+
+// packed row r of the fused QKV matrix -> source row of wq / wk / wv
+// (which = 0 q, 1 k, 2 v; src = row inside that matrix)
+KIE_HD void qkv_source_row(const Dims& m, int r, int* which, int* src) {
+  const int qd = m.H * m.hd, kvd = m.Hkv * m.hd, half = m.hd / 2;
+  if (r < qd + kvd) {
+    const int base = r < qd ? 0 : qd;
+    const int rr = r - base, head = rr / m.hd, j = rr % m.hd;
+    *which = r < qd ? 0 : 1;
+    *src = head * m.hd + (j & 1) * half + (j >> 1);
+  } else {
+    *which = 2;
+    *src = r - qd - kvd;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// workspace (byte offsets from the workspace base)
+//
+// "LL" buffers hold 64-bit words: low 32 bits payload (fp32 bits or an int),
+// high 32 bits the epoch of the decode step that wrote it.  A reader accepts
+// a word only when its epoch is the current step's, so every word carries its
+// own readiness and no separate flag or fence is needed for it.
+// ---------------------------------------------------------------------------
+struct WsLayout {
+  uint64_t state;  // int32[64]: [0] status, [1] abort, [2] token state
+  uint64_t rope;   // float2 [max_ctx][hd/2]  (cos, sin)
+  uint64_t X;      // LL [2L+2][d]     residual stream vectors
+  uint64_t Q;      // LL [L][H hd]     rotated, pre-scaled queries
+  uint64_t KC;     // LL [L][Hkv hd]   current key (fp16-rounded)
+  uint64_t VC;     // LL [L][Hkv hd]   current value (fp16-rounded)
+  uint64_t REC;    // LL [L][nwg][2][G][hd+2]  attention partial records
+  uint64_t OB;     // LL [L][H hd]     merged attention output
+  uint64_t HB;     // LL [L][F]        SwiGLU activations
+  uint64_t LMP;    // LL [nwg][2]      per-workgroup (max logit, argmax)
+  uint64_t ll_begin, ll_end;
+  uint64_t total;
+};
+
+KIE_HD WsLayout ws_layout(const Dims& m, int nwg) {
+  WsLayout w{};
+  uint64_t o = 0;
+  const uint64_t A = 256;
+  w.state = o; o = align_up(o + 256, A);
+  w.rope = o; o = align_up(o + (uint64_t)m.max_ctx * (m.hd / 2) * 8, A);
+  w.ll_begin = o;
+  w.X = o; o = align_up(o + (uint64_t)(2 * m.L + 2) * m.d * 8, A);
+  w.Q = o; o = align_up(o + (uint64_t)m.L * m.H * m.hd * 8, A);
+  w.KC = o; o = align_up(o + (uint64_t)m.L * m.Hkv * m.hd * 8, A);
+  w.VC = o; o = align_up(o + (uint64_t)m.L * m.Hkv * m.hd * 8, A);
+  w.REC = o; o = align_up(o + (uint64_t)m.L * nwg * 2 * m.G * (m.hd + 2) * 8, A);
+  w.OB = o; o = align_up(o + (uint64_t)m.L * m.H * m.hd * 8, A);
+  w.HB = o; o = align_up(o + (uint64_t)m.L * m.F * 8, A);
+  w.LMP = o; o = align_up(o + (uint64_t)nwg * 2 * 8, A);
+  w.ll_end = o;
+  w.total = o;
+  return w;
+}
+
+// KV cache: K[l][g][t][hd] then V[l][g][t][hd], fp16
+KIE_HD uint64_t kv_offset(const Dims& m, int l, int kv, int g) {
+  return (((uint64_t)l * 2 + kv) * m.Hkv + g) * (uint64_t)m.max_ctx * m.hd;
+}
+KIE_HD uint64_t kv_elems(const Dims& m) { return (uint64_t)m.L * 2 * m.Hkv * (uint64_t)m.max_ctx * m.hd; }
+
+// ---------------------------------------------------------------------------
+// partitions
+// ---------------------------------------------------------------------------
+// [a, b) = part i of n items split into `parts` contiguous, balanced pieces
+KIE_HD void split(int n, int parts, int i, int* a, int* b) {
+  *a = (int)(((uint32_t)n * (uint32_t)i) / (uint32_t)parts);
+  *b = (int)(((uint32_t)n * (uint32_t)(i + 1)) / (uint32_t)parts);
+}
+// the part that holds item f (0 <= f < n) under split()
+KIE_HD int split_owner(int f, int n, int parts) {
+  return (int)(((uint32_t)(f + 1) * (uint32_t)parts + (uint32_t)n - 1) / (uint32_t)n) - 1;
+}
+
+// GEMV ops: rows, columns and row grouping of each phase
+struct GemvShape {
+  int rows, K, unit_rows;  // unit_rows rows always stay in one workgroup
+};
+KIE_HD GemvShape gemv_shape(const Dims& m, int kind) {
+  switch (kind) {
+    case PH_QKV: return {(m.H + 2 * m.Hkv) * m.hd, m.d, 2};
+    case PH_O: return {m.d, m.H * m.hd, 1};
+    case PH_GU: return {2 * m.F, m.d, 2};
+    case PH_DOWN: return {m.d, m.F, 1};
+    default: return {m.V, m.d, 1};  // PH_LM
+  }
+}
+KIE_HD int blocks_per_row(int K) { return (K + kBlock - 1) / kBlock; }
+
+// rows [r0, r1) of op `kind` owned by workgroup wg
+KIE_HD void gemv_rows(const Dims& m, int kind, int nwg, int wg, int* r0, int* r1) {
+  GemvShape s = gemv_shape(m, kind);
+  int a, b;
+  split(s.rows / s.unit_rows, nwg, wg, &a, &b);
+  *r0 = a * s.unit_rows;
+  *r1 = b * s.unit_rows;
+}
+
+// the workgroup's rows are cut into units (row, 512-column block); wave w
+// takes units [u0, u1) in row-major order
+KIE_HD void gemv_wave_units(int nrows, int K, int wave, int* u0, int* u1) {
+  split(nrows * blocks_per_row(K), kWaves, wave, u0, u1);
+}
+
+// attention: the n_ctx keys of every KV head are laid end to end
+// (f = g * n_ctx + t) and cut into nwg contiguous ranges; each workgroup range
+// meets at most two heads ("segments"); each segment is cut into kWaves
+// contiguous key ranges, one per wave.
+struct AttnSeg {
+  int g;       // KV head
+  int ta, tb;  // workgroup's keys [ta, tb) of head g
+};
+KIE_HD int attn_segments(int Hkv, int n_ctx, int nwg, int wg, AttnSeg* seg) {
+  int fa, fb;
+  split(Hkv * n_ctx, nwg, wg, &fa, &fb);
+  int n = 0;
+  while (fa < fb && n < 2) {
+    const int g = fa / n_ctx;
+    const int end = (g + 1) * n_ctx < fb ? (g + 1) * n_ctx : fb;
+    seg[n].g = g;
+    seg[n].ta = fa - g * n_ctx;
+    seg[n].tb = end - g * n_ctx;
+    ++n;
+    fa = end;
+  }
+  return n;
+}
+
+// workgroup that holds key t of head g
+KIE_HD int attn_owner(int Hkv, int n_ctx, int nwg, int g, int t) {
+  return split_owner(g * n_ctx + t, Hkv * n_ctx, nwg);
+}
+
+// lanes per key (16 bytes of a key row per lane) and keys per wave load
+KIE_HD int attn_lpk(int hd) { return hd / 8; }
+KIE_HD int attn_kpl(int hd) { return kWave / (hd / 8); }
+
+// per-wave work descriptors kept in LDS (ints):
+//   GEMV kind k (0 QKV, 1 O, 2 GU, 3 DOWN, 4 LM): 8 ints at wave*kWaveDesc + 8k
+//     {offset lo, offset hi (elements from the layer base), b0, n, nb, K8, row0, 0}
+//   attention: 12 ints for the load cursor's step at wave*kWaveDesc + 40 and
+//     12 for the consumer's step at wave*kWaveDesc + 52 (the cursor can be a
+//     step ahead): {g0, ka0, kc0, nst0, pos0, g1, ka1, kc1, nst1, pos1, nseg, merge_g}
+//   workgroup rows per GEMV kind: 2 ints at kWaves*kWaveDesc + 2k {r0, nrows}
+constexpr int kWaveDesc = 64;
+constexpr int kCursorAttn = 40;
+constexpr int kConsumerAttn = 52;
+constexpr int kDescInts = kWaves * kWaveDesc + 16;
+// the kernel's non-ring LDS is one static array of this many floats; a model
+// whose LdsPlan needs more is rejected by the host (the ring adds
+// kWaves x kRingDepth KB)
+constexpr int kMainFloats = 23552;
+constexpr int kRingDepth = 8;
+
+// LDS plan (in floats)
+struct LdsPlan {
+  int xraw, big, gemv_xs, gemv_part, attn_wrec, attn_ml, own, desc;
+  int total_floats;
+  int kmax, rmax, max_recs;
+};
+KIE_HD int imax(int a, int b) { return a > b ? a : b; }
+KIE_HD LdsPlan lds_plan(const Dims& m, int nwg) {
+  LdsPlan p{};
+  int kmax = imax(imax(imax(m.d, m.H * m.hd), m.F), 2 * nwg);
+  kmax = (int)align_up((uint64_t)kmax, kBlock);
+  int rmax = 0;
+  for (int k = 0; k <= PH_LM; ++k) {
+    if (k == PH_ATTN) continue;
+    GemvShape s = gemv_shape(m, k);
+    const int units = s.rows / s.unit_rows;
+    rmax = imax(rmax, ((units + nwg - 1) / nwg) * s.unit_rows);
+  }
+  // records merged for one head: workgroups meeting that head
+  const int max_recs = (nwg + m.Hkv - 1) / m.Hkv + 2;
+  p.kmax = kmax;
+  p.rmax = rmax;
+  p.max_recs = max_recs;
+  int o = 0;
+  p.xraw = o; o += (int)align_up((uint64_t)m.d, 64);
+  p.big = o;
+  p.gemv_xs = o;
+  p.gemv_part = o + kmax;
+  const int gemv_sz = kmax + (int)align_up((uint64_t)rmax * kWaves, 64);
+  p.attn_wrec = o;
+  p.attn_ml = o + 2 * kWaves * m.G * (m.hd + 2);
+  const int attn_sz = 2 * kWaves * m.G * (m.hd + 2) + max_recs * m.G * 4;
+  o += (int)align_up((uint64_t)imax(gemv_sz, attn_sz), 64);
+  p.own = o; o += (int)align_up((uint64_t)2 * ((m.d + nwg - 1) / nwg), 64);
+  p.desc = o; o += kDescInts;
+  p.total_floats = o;
+  return p;
+}
+
+// arguments of one monokernel launch
+struct KParams {
+  Dims m;
+  PackLayout pl;
+  WsLayout wl;
+  LdsPlan lp;
+  const uint16_t* W;  // packed weights
+  uint16_t* kv;       // KV cache
+  uint8_t* ws;        // workspace
+  const int32_t* forced;  // [n_steps] or null
+  int32_t* out;           // [n_steps] or null
+  float* logits;          // [n_steps][V] or null
+  int n_steps, pos0;
+  int lm_mode;            // 0: LM head every step; 1: last step only; 2: never
+  int first_from_state;   // 1: step 0 reads the token state word
+  uint32_t epoch0;        // epoch of step 0
+  uint64_t timeout_ticks; // wall-clock ticks a single wait may take
+  uint32_t debug_flags;
+};
+
+enum DebugFlags : uint32_t {
+  DBG_WAIT_NEVER = 1u,  // workgroup 0 waits on a word no one writes (timeout test)
+};
+
+enum DeviceStatus : int32_t { DEV_OK = 0, DEV_TIMEOUT = 1, DEV_BAD_TOKEN = 2 };
+
+}  // namespace kie

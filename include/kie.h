@@ -1,0 +1,195 @@
+/*
+ * kie.h - C ABI of the MI355X batch-1 fp16 decode monokernel.
+ *
+ * What is computed.  Single-request (batch 1) greedy decoding of a
+ * decoder-only transformer with fp16 weights, run as ONE persistent GPU
+ * kernel per call: prefill, every decode step, the LM head and the greedy
+ * argmax all run inside the kernel without host round trips between layers
+ * or tokens.  This is the problem the Kog Inference Engine pages state
+ * (explainer pages, "Monokernel" bullet of the approach list and the
+ * results table: FP16, batch size 1, no quantization, no speculative
+ * decoding, no pruning, tokens per second per request; Czech explainer,
+ * "Software versus silicon" section: one persistent program running prefill,
+ * decode and LM-head sampling in one go, without per-launch overhead or grid
+ * synchronisations).  The pages do not define the block; this library
+ * implements the Llama-style pre-norm block (RMSNorm, rotate-half RoPE,
+ * causal softmax attention with 1/sqrt(head_dim) scale, SwiGLU, untied
+ * embedding and LM head), and the lane-structured parallel block whose
+ * residual update is delayed by `lane_delay` layers (the pages' Laneformer
+ * lanes with Delayed Tensor Parallelism, delta = 2).
+ *
+ * Numerics: fp16 weights and KV cache; fp32 activations, residual stream and
+ * accumulation; RoPE angles from a table computed in double precision;
+ * greedy argmax takes the lowest token id among equal maxima.
+ *
+ * Memory.  The caller owns every device buffer (allocate with any allocator,
+ * e.g. PyTorch) and keeps it alive while the context uses it; the library
+ * never frees caller memory.  Sizes come from kie_query_sizes().  Host
+ * pointers are read only during the call that receives them.
+ *
+ * Streams.  `stream` arguments are hipStream_t values passed as void*.
+ * Calls are asynchronous on that stream unless stated otherwise; results
+ * are ready after the stream is synchronised.  A context is used by one
+ * thread and one stream at a time.
+ *
+ * Errors.  Every call returns a kie_status; no exception crosses the ABI.
+ * Argument errors are detected on the host before anything is launched.
+ * Errors raised inside the kernel (a bounded wait that timed out, a token
+ * id out of range) are latched in device memory and reported by
+ * kie_sync_status().  kie_last_error() returns a message for the last
+ * failing call on a context.
+ */
+#ifndef KIE_H
+#define KIE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kie_status {
+  KIE_OK = 0,
+  KIE_ERR_INVALID_ARG = -1, /* bad pointer, size or configuration */
+  KIE_ERR_HIP = -2,         /* a HIP runtime call failed */
+  KIE_ERR_CAPACITY = -3,    /* position + tokens would exceed max_ctx */
+  KIE_ERR_STATE = -4,       /* memory not bound / weights not loaded / no device */
+  KIE_ERR_TIMEOUT = -5,     /* a wait inside the kernel exceeded the timeout */
+  KIE_ERR_UNSUPPORTED = -6, /* valid model that this kernel build cannot run */
+  KIE_ERR_BAD_TOKEN = -7    /* a token id outside [0, vocab) reached the kernel */
+} kie_status;
+
+/* Model shape.  Rules (KIE_ERR_INVALID_ARG otherwise): all sizes > 0;
+ * n_heads % n_kv_heads == 0; head_dim even and a multiple of 8;
+ * d_model, n_heads*head_dim and ffn_dim multiples of 8; n_lanes divides
+ * n_heads and ffn_dim; parallel_block in {0,1}; lane_delay >= 0 and 0 when
+ * parallel_block == 0; max_ctx >= 1.  Shapes the kernel cannot hold in LDS
+ * (or a query-group size other than 1, 2, 4) give KIE_ERR_UNSUPPORTED. */
+typedef struct kie_model_config {
+  int32_t n_layers, d_model, n_heads, n_kv_heads, head_dim, ffn_dim, vocab;
+  float rms_eps;      /* added to mean(x^2) inside the square root */
+  double rope_base;   /* theta_i = pos * rope_base^(-2i/head_dim) */
+  int32_t n_lanes;    /* lanes of the parallel block (1 = none) */
+  int32_t lane_delay; /* layers between a layer and the use of its partial */
+  int32_t parallel_block; /* 0: sequential pre-norm block; 1: parallel block */
+  int32_t max_ctx;    /* KV-cache capacity in positions */
+} kie_model_config;
+
+/* Host-side fp16 weights (IEEE binary16 bit patterns), row-major
+ * [out][in] as a Linear layer stores them.  Per-layer members point to
+ * arrays of n_layers pointers.  Shapes: embed, lm_head [vocab][d_model];
+ * final_norm, attn_norm[l], mlp_norm[l] [d_model]; wq[l] [n_heads*hd][d];
+ * wk[l], wv[l] [n_kv_heads*hd][d]; wo[l] [d][n_heads*hd];
+ * w_gate[l], w_up[l] [ffn][d]; w_down[l] [d][ffn]. */
+typedef struct kie_weights {
+  const uint16_t* embed;
+  const uint16_t* lm_head;
+  const uint16_t* final_norm;
+  const uint16_t* const* attn_norm;
+  const uint16_t* const* wq;
+  const uint16_t* const* wk;
+  const uint16_t* const* wv;
+  const uint16_t* const* wo;
+  const uint16_t* const* mlp_norm;
+  const uint16_t* const* w_gate;
+  const uint16_t* const* w_up;
+  const uint16_t* const* w_down;
+} kie_weights;
+
+typedef struct kie_ctx kie_ctx; /* opaque host-side context */
+
+/* Create a context for `cfg` on HIP device `device`.  device < 0 creates a
+ * host-only context (sizes, packing and validation work; anything that needs
+ * a GPU returns KIE_ERR_STATE) that assumes `256` workgroups.
+ * On success *out receives the context; destroy it with kie_destroy(). */
+kie_status kie_create(const kie_model_config* cfg, int device, kie_ctx** out);
+
+/* Bytes of the three caller-owned device buffers: packed weights (every
+ * parameter including the embedding table, laid out for the kernel), the
+ * fp16 KV cache ([n_layers][2][n_kv_heads][max_ctx][head_dim]) and the
+ * workspace (RoPE table, activation exchange words, state).  Any of the
+ * output pointers may be NULL. */
+kie_status kie_query_sizes(const kie_ctx* ctx, size_t* packed_weight_bytes, size_t* kv_bytes,
+                           size_t* workspace_bytes);
+
+/* Bind caller-owned device memory of at least the queried sizes (each
+ * 256-byte aligned).  Initialises the workspace (RoPE table, cleared
+ * exchange words) with a synchronous upload; the KV cache is not cleared.
+ * Rebinding is allowed; it resets the position to 0 and unloads weights. */
+kie_status kie_bind_memory(kie_ctx* ctx, void* d_packed, void* d_kv, void* d_workspace);
+
+/* Pack the host weights into the kernel layout and upload them (blocking
+ * with respect to the host: the host arrays may be freed on return). */
+kie_status kie_load_weights(kie_ctx* ctx, const kie_weights* host_src, void* stream);
+
+/* Run the prompt d_prompt[0..n_prompt) (device int32 ids) at positions
+ * pos..pos+n_prompt-1 (pos is 0 after binding), fill the KV cache and write
+ * the greedy next token t1 to *d_next_token (device, may be NULL) and the
+ * last position's logits [vocab] to d_logits (device fp32, may be NULL).
+ * Afterwards position += n_prompt and t1 is the pending input token.
+ * Long prompts are split into several launches internally. */
+kie_status kie_prefill(kie_ctx* ctx, const int32_t* d_prompt, int32_t n_prompt, int32_t* d_next_token,
+                       float* d_logits, void* stream);
+
+/* Run n_tokens decode steps.  Step k consumes d_forced_in[k] when that
+ * pointer is not NULL (teacher forcing), else the previous step's argmax (the
+ * pending token for k = 0); it runs at position pos + k, writes its greedy
+ * token to d_tokens_out[k] (device, may be NULL) and, when d_logits_out is not
+ * NULL, its logits to d_logits_out[k*vocab .. (k+1)*vocab).  Afterwards
+ * position += n_tokens and the last emitted token is pending.
+ * KIE_ERR_CAPACITY if position + n_tokens > max_ctx. */
+kie_status kie_decode(kie_ctx* ctx, int32_t n_tokens, int32_t* d_tokens_out, const int32_t* d_forced_in,
+                      float* d_logits_out, void* stream);
+
+/* Set the position (0 <= pos <= max_ctx) and the pending input token
+ * (0 <= token < vocab) without touching the KV cache, e.g. to time the same
+ * decode again.  Asynchronous on `stream`. */
+kie_status kie_set_position(kie_ctx* ctx, int32_t pos, int32_t next_token, void* stream);
+
+/* Synchronise `stream` and report errors latched by the kernel
+ * (KIE_ERR_TIMEOUT, KIE_ERR_BAD_TOKEN), clearing them. */
+kie_status kie_sync_status(kie_ctx* ctx, void* stream);
+
+/* Longest time one wait inside the kernel may take before the launch gives
+ * up with KIE_ERR_TIMEOUT (default 2 000 000 us). */
+kie_status kie_set_timeout_us(kie_ctx* ctx, uint64_t microseconds);
+
+/* Debug flags (bit 0: one workgroup waits on a word nobody writes, which
+ * must end in KIE_ERR_TIMEOUT, not a hang).  0 = normal operation. */
+kie_status kie_set_debug_flags(kie_ctx* ctx, uint32_t flags);
+
+/* Most decode steps one launch runs before the library starts the next one
+ * (default 512); keeps each launch short. */
+kie_status kie_set_launch_steps(kie_ctx* ctx, int32_t steps);
+
+/* CPU-only: write the packed layout of `src` for `cfg` into host_dst
+ * (packed_weight_bytes from kie_query_sizes of any context for cfg). */
+kie_status kie_pack_weights_host(const kie_model_config* cfg, const kie_weights* src, void* host_dst);
+
+/* Launch shape: workgroups (= compute units), threads per workgroup, LDS
+ * bytes per workgroup, KV-cache positions per wave load, and the packed
+ * element offsets of layer 0's fused QKV matrix and the LM head. */
+kie_status kie_launch_info(const kie_ctx* ctx, int32_t* n_workgroups, int32_t* threads, int32_t* lds_bytes,
+                           int64_t* qkv_offset, int64_t* lm_offset);
+
+/* CPU-only: check the work partition the kernel derives for `cfg` on
+ * n_workgroups workgroups at context length n_ctx: every GEMV row and
+ * every 512-column block of it belongs to exactly one wave, every attention
+ * key of every KV head to exactly one wave, every head has exactly one merging
+ * workgroup and every workgroup meets at most two heads.  On failure returns
+ * KIE_ERR_INVALID_ARG and writes a message into msg (msg_len bytes). */
+kie_status kie_validate_schedule(const kie_model_config* cfg, int32_t n_workgroups, int32_t n_ctx, char* msg,
+                                 size_t msg_len);
+
+/* Current position (number of cached positions). */
+int32_t kie_position(const kie_ctx* ctx);
+
+const char* kie_status_string(kie_status s);
+const char* kie_last_error(const kie_ctx* ctx);
+void kie_destroy(kie_ctx* ctx);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KIE_H */

@@ -1,0 +1,65 @@
+"""Shared helpers of the GPU parity tests: run the oracle and the HIP path on
+the same seeded inputs and compare them step by step.
+
+Bar (per decode step and for the prefill's last position): relative L2 error
+of the logits <= 1e-3, and the same greedy token wherever the oracle's
+top-1 / top-2 margin exceeds 1e-2 (where it does not, both tokens are
+correct answers to the fp16 problem)."""
+from __future__ import annotations
+
+import sys
+import time
+
+import numpy as np
+
+REL_TOL = 1e-3
+MARGIN = 1e-2
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def rel_l2(a, b) -> float:
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    return float(np.linalg.norm(a - b) / np.linalg.norm(b))
+
+
+def margin(lg) -> float:
+    top = np.partition(np.asarray(lg, dtype=np.float64), -2)[-2:]
+    return float(top[1] - top[0])
+
+
+def compare_step(ref_logits, gpu_logits, gpu_token):
+    r = rel_l2(gpu_logits, ref_logits)
+    m = margin(ref_logits)
+    ref_tok = int(np.argmax(ref_logits))
+    tok_ok = (m <= MARGIN) or (int(gpu_token) == ref_tok)
+    # the GPU's own token must be the argmax of the logits it returned
+    self_ok = int(gpu_token) == int(np.argmax(gpu_logits))
+    return r, tok_ok, self_ok, m
+
+
+def teacher_forced(cfg, weights, prompt, n_steps, engine_factory, oracle_factory, ref=None):
+    """returns (report dict, engine) -- engine left open for further checks"""
+    t0 = time.time()
+    if ref is None:
+        ref = oracle_factory(cfg, weights).run(prompt, n_steps)
+    t_or = time.time() - t0
+    eng = engine_factory(cfg, len(prompt) + n_steps)
+    eng.load_weights(weights)
+    t1, lg0 = eng.prefill(prompt, want_logits=True)
+    toks, lgs = eng.decode(n_steps, forced=ref["inputs"], want_logits=True)
+    worst = rel_l2(lg0, ref["prefill_logits"])
+    bad_tok = 0 if (margin(ref["prefill_logits"]) <= MARGIN or t1 == ref["t1"]) else 1
+    bad_self = 0
+    for k in range(n_steps):
+        r, tok_ok, self_ok, _ = compare_step(ref["logits"][k], lgs[k], toks[k])
+        worst = max(worst, r)
+        bad_tok += 0 if tok_ok else 1
+        bad_self += 0 if self_ok else 1
+    rep = dict(worst_rel=worst, bad_tokens=bad_tok, bad_self=bad_self, n=n_steps, oracle_s=t_or,
+               t1=t1, ref_t1=ref["t1"], toks=toks, logits=lgs, ref=ref)
+    return rep, eng

@@ -1,0 +1,164 @@
+"""GPU parity of the HIP decode path against the fp64 oracle (through the C ABI).
+
+Every test prints its case before touching the GPU.  Each model here is small
+enough for the oracle to follow every step; the large configurations are in
+test_gpu_large.py."""
+import numpy as np
+import pytest
+
+from decode_persistent_monokernel_amd.config import CFG0
+from decode_persistent_monokernel_amd.inputs import gen_weights, gen_prompt
+from oracle import Oracle
+from paritylib import REL_TOL, say, teacher_forced, rel_l2
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - CPU container
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+from decode_persistent_monokernel_amd.kie import Engine, KieError  # noqa: E402
+
+
+def make_engine(cfg, max_ctx):
+    e = Engine(cfg, device=0, max_ctx=max_ctx)
+    e.set_timeout_us(2_000_000)
+    return e
+
+
+def check(rep, name):
+    say(f"[{name}] worst rel-L2 {rep['worst_rel']:.3e}  token mismatches(margin>1e-2) {rep['bad_tokens']}"
+        f"  self-argmax mismatches {rep['bad_self']}  t1 {rep['t1']}/{rep['ref_t1']}")
+    assert rep["worst_rel"] <= REL_TOL
+    assert rep["bad_tokens"] == 0
+    assert rep["bad_self"] == 0
+
+
+def test_cfg0_teacher_forced():
+    cfg = CFG0
+    say(f"case cfg0 full: P={cfg.prompt_len} N={cfg.decode_steps}")
+    w = gen_weights(cfg)
+    rep, eng = teacher_forced(cfg, w, gen_prompt(cfg), cfg.decode_steps, make_engine, Oracle)
+    check(rep, "cfg0")
+    eng.close()
+
+
+def test_cfg0_peaky_attention():
+    """Wq, Wk with std 0.2 make the softmax sharp, so a misplaced key moves the
+    logits (at std 0.02 attention is nearly uniform and hides such bugs)"""
+    cfg = CFG0.with_(seed_index=10)
+    say("case cfg0 peaky attention (wq, wk std 0.2)")
+    w = gen_weights(cfg, overrides={"wq": 0.2, "wk": 0.2})
+    rep, eng = teacher_forced(cfg, w, gen_prompt(cfg), cfg.decode_steps, make_engine, Oracle)
+    check(rep, "cfg0-peaky")
+    eng.close()
+
+
+@pytest.mark.parametrize("shape", [
+    dict(n_heads=8, n_kv_heads=2, head_dim=32, name="gqa4"),
+    dict(n_heads=8, n_kv_heads=4, head_dim=32, name="gqa2"),
+    dict(d_model=320, n_heads=4, n_kv_heads=4, head_dim=80, ffn_dim=864, name="hd80"),
+    dict(d_model=384, n_heads=6, n_kv_heads=6, head_dim=64, ffn_dim=1536, vocab=1000, name="ragged"),
+], ids=lambda s: s["name"])
+def test_small_shapes_teacher_forced(shape):
+    cfg = CFG0.with_(seed_index=11, prompt_len=9, decode_steps=12, **shape)
+    say(f"case small shape {shape}")
+    w = gen_weights(cfg, overrides={"wq": 0.1, "wk": 0.1})
+    rep, eng = teacher_forced(cfg, w, gen_prompt(cfg), cfg.decode_steps, make_engine, Oracle)
+    check(rep, shape["name"])
+    eng.close()
+
+
+def test_lane_block_small():
+    cfg = CFG0.with_(name="lanes", n_layers=5, n_lanes=2, lane_delay=2, sequential=False, seed_index=12,
+                     prompt_len=7, decode_steps=10)
+    say("case parallel block, delay 2, 5 layers")
+    w = gen_weights(cfg, overrides={"wq": 0.1, "wk": 0.1})
+    rep, eng = teacher_forced(cfg, w, gen_prompt(cfg), cfg.decode_steps, make_engine, Oracle)
+    check(rep, "lanes-small")
+    eng.close()
+
+
+def test_single_token_prompt_and_free_running():
+    cfg = CFG0.with_(seed_index=13, prompt_len=1, decode_steps=20)
+    say("case prompt of one token, free-running greedy")
+    w = gen_weights(cfg)
+    prompt = gen_prompt(cfg)
+    ref = Oracle(cfg, w).run(prompt, cfg.decode_steps)
+    eng = make_engine(cfg, cfg.max_ctx)
+    eng.load_weights(w)
+    t1 = eng.prefill(prompt)
+    toks, lgs = eng.decode(cfg.decode_steps, want_logits=True)
+    # free running: agree while every oracle step is decisive
+    for k in range(cfg.decode_steps):
+        lg = ref["logits"][k]
+        top = np.sort(lg)[-2:]
+        if top[1] - top[0] <= 1e-2:
+            break
+        assert toks[k] == ref["tokens"][k], k
+        assert rel_l2(lgs[k], lg) <= REL_TOL
+    assert t1 == ref["t1"]
+    eng.close()
+
+
+def test_deterministic_and_resumable():
+    """bitwise-identical logits on a repeat, and decode(a) + decode(b) == decode(a + b)"""
+    cfg = CFG0.with_(seed_index=14, prompt_len=11, decode_steps=24)
+    say("case determinism / resume")
+    w = gen_weights(cfg)
+    prompt = gen_prompt(cfg)
+    eng = make_engine(cfg, cfg.max_ctx)
+    eng.load_weights(w)
+    t1 = eng.prefill(prompt)
+    a_tok, a_lg = eng.decode(24, want_logits=True)
+    eng.set_position(len(prompt), t1)
+    b_tok, b_lg = eng.decode(24, want_logits=True)
+    assert np.array_equal(a_tok, b_tok) and np.array_equal(a_lg.view(np.uint32), b_lg.view(np.uint32))
+    eng.set_position(len(prompt), t1)
+    c1, l1 = eng.decode(9, want_logits=True)
+    c2, l2 = eng.decode(15, want_logits=True)
+    assert np.array_equal(np.concatenate([c1, c2]), a_tok)
+    assert np.array_equal(np.concatenate([l1, l2]).view(np.uint32), a_lg.view(np.uint32))
+    # launches split into short chunks give the same bits
+    eng.set_position(len(prompt), t1)
+    eng.set_launch_steps(5)
+    d_tok, d_lg = eng.decode(24, want_logits=True)
+    assert np.array_equal(d_lg.view(np.uint32), a_lg.view(np.uint32))
+    eng.close()
+
+
+def test_bounded_wait_reports_timeout():
+    """a workgroup waits on a word nobody writes: the launch must end with
+    KIE_ERR_TIMEOUT, not hang, and the context must work again afterwards"""
+    cfg = CFG0.with_(seed_index=15, prompt_len=4, decode_steps=4)
+    say("case forced timeout (bounded wait)")
+    w = gen_weights(cfg)
+    eng = make_engine(cfg, cfg.max_ctx)
+    eng.load_weights(w)
+    t1 = eng.prefill(gen_prompt(cfg))
+    eng.set_timeout_us(20_000)
+    eng.set_debug_flags(1)
+    with pytest.raises(KieError) as ei:
+        eng.decode(2)
+    assert ei.value.status == -5
+    eng.set_debug_flags(0)
+    eng.set_timeout_us(2_000_000)
+    eng.set_position(cfg.prompt_len, t1)
+    toks = eng.decode(2)
+    assert toks.shape == (2,)
+    eng.close()
+
+
+def test_capacity_and_bad_token_errors():
+    cfg = CFG0.with_(seed_index=16, prompt_len=4, decode_steps=4)
+    say("case capacity / bad token")
+    eng = make_engine(cfg, cfg.max_ctx)
+    eng.load_weights(gen_weights(cfg))
+    eng.prefill(gen_prompt(cfg))
+    with pytest.raises(KieError) as ei:
+        eng.decode(cfg.max_ctx)
+    assert ei.value.status == -3
+    with pytest.raises(KieError) as ei:
+        eng.decode(1, forced=[cfg.vocab + 5])
+    assert ei.value.status == -7
+    eng.close()

@@ -1,0 +1,174 @@
+"""Host logic of the C ABI, on the CPU: the library loads and exports every
+declared symbol, configurations are validated, buffer sizes follow the
+layout, the packer is a pure permutation of the weights, and the kernel's work
+partition covers every row and key exactly once."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+from decode_persistent_monokernel_amd import kie
+from decode_persistent_monokernel_amd.config import CFG0, CFG1, CFG2, CFG3, CFG4, ModelConfig
+from decode_persistent_monokernel_amd.inputs import gen_weights
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kie.h")
+
+needs_lib = pytest.mark.skipif(not os.path.exists(kie.LIB_PATH), reason="libkie.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kie_[a-z_]+)\s*\(", text)))
+
+
+@needs_lib
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert len(names) >= 18
+    L = C.CDLL(kie.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+@needs_lib
+@pytest.mark.parametrize("cfg", [CFG0, CFG1, CFG2, CFG3, CFG4], ids=lambda c: c.name)
+def test_presets_are_accepted_host_only(cfg):
+    assert kie.create_status(cfg, -1) == kie.KIE_OK
+
+
+@needs_lib
+@pytest.mark.parametrize("bad", [
+    dict(n_layers=0), dict(n_heads=6, n_kv_heads=4), dict(head_dim=60), dict(ffn_dim=1020),
+    dict(n_lanes=3), dict(lane_delay=2), dict(vocab=-1), dict(rope_base=1.0),
+])
+def test_invalid_configs_rejected(bad):
+    assert kie.create_status(CFG0.with_(**bad), -1) == -1
+
+
+@needs_lib
+def test_unsupported_shapes_rejected():
+    # 8 query heads per KV head and an FFN too wide for the LDS plan
+    assert kie.create_status(CFG0.with_(n_heads=8, n_kv_heads=1, d_model=512), -1) == -6
+    assert kie.create_status(CFG0.with_(ffn_dim=32768), -1) == -6
+
+
+@needs_lib
+def test_sizes_follow_layout():
+    for cfg in (CFG0, CFG2, CFG4):
+        packed, kvb, ws = kie.query_sizes(cfg)
+        params = cfg.param_elems() * 2
+        assert params <= packed <= params + 4096 * (9 * cfg.n_layers + 3)
+        assert kvb == cfg.n_layers * 2 * cfg.n_kv_heads * cfg.max_ctx * cfg.head_dim * 2
+        assert ws > cfg.max_ctx * cfg.head_dim * 4  # holds the RoPE table
+
+
+@needs_lib
+def test_host_only_context_refuses_gpu_calls():
+    L = kie.lib()
+    ctx = C.c_void_p()
+    c = kie.config_c(CFG0)
+    assert L.kie_create(C.byref(c), -1, C.byref(ctx)) == 0
+    try:
+        assert L.kie_bind_memory(ctx, 256, 256, 256) == -4
+        assert L.kie_decode(ctx, 1, None, None, None, None) == -4
+        assert L.kie_prefill(ctx, 256, 1, None, None, None) == -4
+        assert L.kie_set_timeout_us(ctx, 0) == -1
+        assert L.kie_set_launch_steps(ctx, 0) == -1
+        assert L.kie_position(ctx) == 0
+        assert L.kie_status_string(-5) == b"wait timed out inside the kernel"
+    finally:
+        L.kie_destroy(ctx)
+
+
+def _unpack(cfg: ModelConfig, packed: np.ndarray, offsets):
+    """invert the packed layout with the layout rules written out here"""
+    d, H, Hkv, hd, F = cfg.d_model, cfg.n_heads, cfg.n_kv_heads, cfg.head_dim, cfg.ffn_dim
+    out = {}
+    stride = offsets["layer_stride"]
+    for l in range(cfg.n_layers):
+        base = l * stride
+        g = lambda off, n: packed[base + off: base + off + n]
+        out[f"layers.{l}.attn_norm"] = g(offsets["attn_norm"], d)
+        qkv = g(offsets["wqkv"], (H + 2 * Hkv) * hd * d).reshape(-1, d)
+        def unperm(block, heads):
+            blk = block.reshape(heads, hd, d)
+            o = np.empty_like(blk)
+            o[:, : hd // 2] = blk[:, 0::2]
+            o[:, hd // 2:] = blk[:, 1::2]
+            return o.reshape(heads * hd, d)
+        out[f"layers.{l}.wq"] = unperm(qkv[: H * hd], H)
+        out[f"layers.{l}.wk"] = unperm(qkv[H * hd: (H + Hkv) * hd], Hkv)
+        out[f"layers.{l}.wv"] = qkv[(H + Hkv) * hd:]
+        out[f"layers.{l}.wo"] = g(offsets["wo"], d * H * hd).reshape(d, H * hd)
+        out[f"layers.{l}.mlp_norm"] = g(offsets["mlp_norm"], d)
+        gu = g(offsets["wgu"], 2 * F * d).reshape(2 * F, d)
+        out[f"layers.{l}.w_gate"] = gu[0::2]
+        out[f"layers.{l}.w_up"] = gu[1::2]
+        out[f"layers.{l}.w_down"] = g(offsets["wd"], d * F).reshape(d, F)
+    out["final_norm"] = packed[offsets["final_norm"]: offsets["final_norm"] + d]
+    out["lm_head"] = packed[offsets["lm_head"]: offsets["lm_head"] + cfg.vocab * d].reshape(cfg.vocab, d)
+    out["embed"] = packed[offsets["embed"]: offsets["embed"] + cfg.vocab * d].reshape(cfg.vocab, d)
+    return out
+
+
+def _offsets(cfg):
+    """256-byte aligned offsets (elements), written from the layout rules"""
+    a = lambda x: (x + 127) // 128 * 128
+    d, qd, kvd, F = cfg.d_model, cfg.q_dim, cfg.kv_dim, cfg.ffn_dim
+    o = {}
+    x = 0
+    o["attn_norm"] = x; x = a(x + d)
+    o["wqkv"] = x; x = a(x + (qd + 2 * kvd) * d)
+    o["wo"] = x; x = a(x + d * qd)
+    o["mlp_norm"] = x; x = a(x + d)
+    o["wgu"] = x; x = a(x + 2 * F * d)
+    o["wd"] = x; x = a(x + d * F)
+    o["layer_stride"] = x
+    x = x * cfg.n_layers
+    o["final_norm"] = x; x = a(x + d)
+    o["lm_head"] = x; x = a(x + cfg.vocab * d)
+    o["embed"] = x
+    return o
+
+
+@needs_lib
+@pytest.mark.parametrize("cfg", [
+    CFG0.with_(n_layers=2, vocab=512),
+    CFG0.with_(n_layers=1, n_heads=8, n_kv_heads=2, head_dim=32, vocab=300, name="gqa"),
+    CFG3.with_(n_layers=1, d_model=320, n_heads=4, n_kv_heads=4, head_dim=80, ffn_dim=864, vocab=100, n_lanes=4),
+], ids=["mha", "gqa", "hd80"])
+def test_packer_is_a_permutation(cfg):
+    w = gen_weights(cfg, std=0.5, threads=2)
+    # distinct, recognisable norms
+    for l in range(cfg.n_layers):
+        w[f"layers.{l}.attn_norm"] = (np.arange(cfg.d_model) % 7 + 1).astype(np.float16)
+        w[f"layers.{l}.mlp_norm"] = (np.arange(cfg.d_model) % 5 + 2).astype(np.float16)
+    packed = kie.pack_weights_host(cfg, w)
+    off = _offsets(cfg)
+    assert packed.size * 2 >= (off["embed"] + cfg.vocab * cfg.d_model) * 2
+    back = _unpack(cfg, packed, off)
+    for k, v in w.items():
+        assert np.array_equal(back[k], v.view(np.uint16)), k
+
+
+@needs_lib
+@pytest.mark.parametrize("cfg", [CFG0, CFG1, CFG2, CFG3, CFG4], ids=lambda c: c.name)
+def test_schedule_covers_everything(cfg):
+    ctxs = sorted({1, 2, 3, 17, cfg.prompt_len, cfg.prompt_len + 1, cfg.max_ctx})
+    for nwg in (256, 80, 304):
+        for n in ctxs:
+            try:
+                kie.validate_schedule(cfg, nwg, n)
+            except kie.KieError as e:
+                # fewer workgroups can leave too many LM-head rows for the LDS plan
+                assert nwg < 256 and "LDS" in str(e), str(e)
+
+
+@needs_lib
+def test_schedule_validator_reports_problems():
+    with pytest.raises(kie.KieError):
+        kie.validate_schedule(CFG0, 2, 5)  # fewer workgroups than KV heads
