@@ -303,7 +303,7 @@ KIE_DI void cursor_enter(const Dev& D, Cursor& c) {
   c.kind = kind;
   c.l = l;
   if (kind == PH_ATTN) {
-    const int* a = D.desc + D.wave * kWaveDesc + kCursorAttn;
+    const int* a = D.desc + D.wave * kWaveDesc + kConsumerAttn;
     const int nst0 = a[3], nst1 = a[8];
     const bool first = nst0 > 0;
     const int g = first ? a[0] : a[5];
@@ -327,21 +327,15 @@ KIE_DI void cursor_enter(const Dev& D, Cursor& c) {
   c.K8 = g[5];
 }
 
+// The cursor never crosses into the next step by itself: the next step reads
+// KV-cache rows written during this step, which are only visible after the
+// end-of-step acquire.  At the end of its step it issues harmless loads until
+// the consumer restarts it (cursor_restart) after that acquire.
 KIE_DI void cursor_advance(const Dev& D, Cursor& c) {
-  const KParams& p = *D.p;
   while (c.rem == 0 && !c.done) {
     if (++c.ph >= c.nph) {
-      if (++c.s >= p.n_steps) {
-        c.done = 1;
-        break;
-      }
-      c.ph = 0;
-      c.nph = nphases(p, c.s);
-      // the cursor's own attention descriptor for its new step
-      int ad[12];
-      write_attn_desc(p, D.nwg, D.wg, D.wave, D.kpl, p.pos0 + c.s, ad);
-#pragma unroll
-      for (int i = 0; i < 12; ++i) D.desc[D.wave * kWaveDesc + kCursorAttn + i] = ad[i];
+      c.done = 1;
+      break;
     }
     cursor_enter(D, c);
   }
@@ -361,7 +355,7 @@ KIE_DI void cursor_issue(const Dev& D, Cursor& c, int slot) {
       if (D.lane_active && key < c.kc) a = (const uint4*)((c.kvh ? c.vb : c.kb) + (uint64_t)key * p.m.hd) + D.dl;
       if (c.kvh) {
         if (++c.st == c.nst && c.seg1) {
-          const int* s1 = D.desc + D.wave * kWaveDesc + kCursorAttn + 5;
+          const int* s1 = D.desc + D.wave * kWaveDesc + kConsumerAttn + 5;
           c.seg1 = 0;
           c.st = 0;
           c.ka = s1[1];
@@ -572,21 +566,15 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
         }
       }
     }
-    int ad[12];
-    write_attn_desc(p, D.nwg, D.wg, D.wave, D.kpl, p.pos0, ad);
-    if (D.lane == 0) {
-#pragma unroll
-      for (int i = 0; i < 12; ++i) D.desc[D.wave * kWaveDesc + kCursorAttn + i] = ad[i];
-    }
   }
   __syncthreads();
 
-  // cursor and ring
+  // cursor and ring (started at the top of every step)
   Cursor cur;
   cur.s = 0;
   cur.ph = 0;
-  cur.nph = nphases(p, 0);
-  cur.done = p.n_steps <= 0;
+  cur.nph = 0;
+  cur.done = 1;
   cur.rem = 0;
   cur.kind = PH_QKV;
   cur.st = 0; cur.kvh = 0; cur.ka = 0; cur.kc = 0; cur.nst = 0; cur.seg1 = 0; cur.l = 0;
@@ -594,8 +582,6 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
   cur.rowp = (const uint4*)p.W;
   cur.kb = p.kv;
   cur.vb = p.kv;
-  if (!cur.done) cursor_enter(D, cur);
-  for (int i = 0; i < kDepth; ++i) cursor_issue(D, cur, i);
   int slot = 0;
 
   int token = 0;
@@ -603,7 +589,7 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
   for (int s = 0; s < p.n_steps; ++s) {
     const uint32_t epoch = p.epoch0 + (uint32_t)s;
     const int pos = p.pos0 + s;
-    // the consumer's attention descriptor for this step
+    // this step's attention descriptor (read by the consumer and the cursor)
     int* adesc = D.desc + D.wave * kWaveDesc + kConsumerAttn;
     {
       int ad[12];
@@ -611,6 +597,16 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
 #pragma unroll
       for (int i = 0; i < 12; ++i) adesc[i] = ad[i];
     }
+    // restart the cursor on this step and fill the ring.  Every earlier ring
+    // load has completed (the end-of-step polls waited for them), so the
+    // slots can be reused in order from `slot`.
+    __builtin_amdgcn_s_waitcnt(kWaitAllVm);
+    cur.s = s;
+    cur.ph = 0;
+    cur.nph = nphases(p, s);
+    cur.done = 0;
+    cursor_enter(D, cur);
+    for (int i = 0; i < kDepth; ++i) cursor_issue(D, cur, slot + i < kDepth ? slot + i : slot + i - kDepth);
 
     // ---- input token and embedding ------------------------------------
     if (p.forced) {
@@ -712,7 +708,10 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
               if (mine) online_update(mrow[h], lrow[h], acc[h], t, vx);
             }
           }
-          // merge this wave's key slots into lanes 0..lpk-1
+          // merge this wave's key slots into lanes 0..lpk-1.  Only those
+          // lanes accumulate; every other lane keeps its own slot's state, so
+          // each slot is counted exactly once.
+          const bool dst = D.lane < D.lpk;
           for (int k = 1; k < D.kpl; ++k) {
             const int src = D.lane + k * D.lpk;
 #pragma unroll
@@ -722,7 +721,7 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
               float ao[8];
 #pragma unroll
               for (int e = 0; e < 8; ++e) ao[e] = __shfl(acc[h][e], src);
-              lse_merge(mrow[h], lrow[h], acc[h], mo, lo, ao);
+              if (dst) lse_merge(mrow[h], lrow[h], acc[h], mo, lo, ao);
             }
           }
           if (D.lane < D.lpk) {

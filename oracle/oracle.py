@@ -120,8 +120,12 @@ class Oracle:
     ffn_dim, vocab, rms_eps, rope_base, lane_delay, sequential, n_lanes.
     weights: dict of float16 arrays named as by the input generator."""
 
-    def __init__(self, cfg, weights: Dict[str, np.ndarray]):
+    def __init__(self, cfg, weights: Dict[str, np.ndarray], kv_fp16: bool = False):
+        """kv_fp16: store K and V in the cache rounded to binary16 (round to
+        nearest even), the cache of an FP16 model; arithmetic stays fp64.
+        Default: the cache keeps fp64 values."""
         self.cfg = cfg
+        self.kv_fp16 = bool(kv_fp16)
         up = lambda a: np.asarray(a).astype(f64)
         self.embed16 = weights["embed"]
         self.layers: List[Layer] = []
@@ -141,6 +145,9 @@ class Oracle:
         self.delay = int(getattr(cfg, "lane_delay", 0))
 
     # -- helpers ---------------------------------------------------------
+    def cache_round(self, a: np.ndarray) -> np.ndarray:
+        return a.astype(np.float16).astype(f64) if self.kv_fp16 else a
+
     def embed(self, tokens) -> np.ndarray:
         return self.embed16[np.asarray(tokens)].astype(f64)
 
@@ -212,8 +219,8 @@ class Oracle:
         for l, L in enumerate(self.layers):
             h = rmsnorm(x, L.attn_norm, self.eps)
             q, k, v = self.qkv(L, h, pos)
-            cache.K[l][:, start:start + n, :] = k.transpose(1, 0, 2)
-            cache.V[l][:, start:start + n, :] = v.transpose(1, 0, 2)
+            cache.K[l][:, start:start + n, :] = self.cache_round(k.transpose(1, 0, 2))
+            cache.V[l][:, start:start + n, :] = self.cache_round(v.transpose(1, 0, 2))
             kk = cache.K[l][:, :start + n, :].transpose(1, 0, 2)
             vv = cache.V[l][:, :start + n, :].transpose(1, 0, 2)
             a = self.causal_attention(q, kk, vv, pos).reshape(n, -1) @ L.wo.T
@@ -236,8 +243,8 @@ class Oracle:
         for l, L in enumerate(self.layers):
             h = rmsnorm(x, L.attn_norm, self.eps)
             q, k, v = self.qkv(L, h[None, :], np.array([pos]))
-            cache.K[l][:, pos, :] = k[0]
-            cache.V[l][:, pos, :] = v[0]
+            cache.K[l][:, pos, :] = self.cache_round(k[0])
+            cache.V[l][:, pos, :] = self.cache_round(v[0])
             o = np.empty((self.H, self.hd))
             for i in range(self.H):
                 g = i // self.G

@@ -54,8 +54,15 @@ def silu(z):
     return z / (1.0 + math.exp(-z))
 
 
+def to_half(x):
+    """round a Python float to the nearest binary16 value (ties to even)"""
+    import struct
+    return struct.unpack("<e", struct.pack("<e", x))[0]
+
+
 class BruteDecoder:
-    def __init__(self, cfg, weights):
+    def __init__(self, cfg, weights, kv_fp16=False):
+        self.kv_fp16 = kv_fp16
         self.c = cfg
         self.w = {k: tolist(v) for k, v in weights.items()}
         self.K = [[[] for _ in range(cfg.n_kv_heads)] for _ in range(cfg.n_layers)]
@@ -72,9 +79,10 @@ class BruteDecoder:
         q = matvec(self.lw(l, "wq"), h)
         k = matvec(self.lw(l, "wk"), h)
         v = matvec(self.lw(l, "wv"), h)
+        rnd = to_half if self.kv_fp16 else (lambda t: t)
         for g in range(Hkv):
-            self.K[l][g].append(rope(k[g * hd:(g + 1) * hd], pos, c.rope_base))
-            self.V[l][g].append(v[g * hd:(g + 1) * hd])
+            self.K[l][g].append([rnd(t) for t in rope(k[g * hd:(g + 1) * hd], pos, c.rope_base)])
+            self.V[l][g].append([rnd(t) for t in v[g * hd:(g + 1) * hd]])
         o = []
         for i in range(H):
             qi = rope(q[i * hd:(i + 1) * hd], pos, c.rope_base)

@@ -43,14 +43,34 @@ def test_cfg0_teacher_forced():
     eng.close()
 
 
+def oracle_fp16_cache(cfg, w):
+    """the oracle with K/V rounded to binary16 in the cache (the cache of an
+    FP16 model); used where sharp attention would let the fp16 rounding of
+    the cached keys alone exceed the bar against the fp64-cache oracle"""
+    return Oracle(cfg, w, kv_fp16=True)
+
+
 def test_cfg0_peaky_attention():
     """Wq, Wk with std 0.2 make the softmax sharp, so a misplaced key moves the
     logits (at std 0.02 attention is nearly uniform and hides such bugs)"""
     cfg = CFG0.with_(seed_index=10)
     say("case cfg0 peaky attention (wq, wk std 0.2)")
     w = gen_weights(cfg, overrides={"wq": 0.2, "wk": 0.2})
-    rep, eng = teacher_forced(cfg, w, gen_prompt(cfg), cfg.decode_steps, make_engine, Oracle)
+    rep, eng = teacher_forced(cfg, w, gen_prompt(cfg), cfg.decode_steps, make_engine, oracle_fp16_cache)
     check(rep, "cfg0-peaky")
+    eng.close()
+
+
+@pytest.mark.parametrize("hd,H,d", [(64, 4, 256), (80, 4, 320), (128, 2, 256), (32, 8, 256)])
+def test_many_keys_per_wave(hd, H, d):
+    """a 2.5K-token context spreads 4..20 keys over every wave, so every key
+    slot of the split-context attention and its merges are exercised"""
+    cfg = CFG0.with_(seed_index=17, d_model=d, n_heads=H, n_kv_heads=H, head_dim=hd, prompt_len=2500,
+                     decode_steps=4, vocab=2048)
+    say(f"case long context hd={hd} H={H} P=2500")
+    w = gen_weights(cfg, overrides={"wq": 0.12, "wk": 0.12})
+    rep, eng = teacher_forced(cfg, w, gen_prompt(cfg), cfg.decode_steps, make_engine, oracle_fp16_cache)
+    check(rep, f"long-hd{hd}")
     eng.close()
 
 
@@ -64,7 +84,7 @@ def test_small_shapes_teacher_forced(shape):
     cfg = CFG0.with_(seed_index=11, prompt_len=9, decode_steps=12, **shape)
     say(f"case small shape {shape}")
     w = gen_weights(cfg, overrides={"wq": 0.1, "wk": 0.1})
-    rep, eng = teacher_forced(cfg, w, gen_prompt(cfg), cfg.decode_steps, make_engine, Oracle)
+    rep, eng = teacher_forced(cfg, w, gen_prompt(cfg), cfg.decode_steps, make_engine, oracle_fp16_cache)
     check(rep, shape["name"])
     eng.close()
 
@@ -74,7 +94,7 @@ def test_lane_block_small():
                      prompt_len=7, decode_steps=10)
     say("case parallel block, delay 2, 5 layers")
     w = gen_weights(cfg, overrides={"wq": 0.1, "wk": 0.1})
-    rep, eng = teacher_forced(cfg, w, gen_prompt(cfg), cfg.decode_steps, make_engine, Oracle)
+    rep, eng = teacher_forced(cfg, w, gen_prompt(cfg), cfg.decode_steps, make_engine, oracle_fp16_cache)
     check(rep, "lanes-small")
     eng.close()
 

@@ -30,12 +30,12 @@ def rel(a, b):
 # ----------------------------------------------------------------------------
 # checks
 # ----------------------------------------------------------------------------
-def check_bruteforce(cfg, std=0.5, n_steps=3):
+def check_bruteforce(cfg, std=0.5, n_steps=3, kv_fp16=False):
     w = gen_weights(cfg, std=std, threads=1)
     prompt = gen_prompt(cfg)
-    orc = O.Oracle(cfg, w)
+    orc = O.Oracle(cfg, w, kv_fp16=kv_fp16)
     res = orc.run(prompt, n_steps)
-    bf = BruteDecoder(cfg, w)
+    bf = BruteDecoder(cfg, w, kv_fp16=kv_fp16)
     worst = 0.0
     lg = None
     for p, t in enumerate(prompt):
@@ -121,6 +121,18 @@ def check_argmax_ties():
 @pytest.mark.parametrize("cfg", [TINY, TINY_GQA, TINY_LANES], ids=lambda c: c.name)
 def test_bruteforce_tiny(cfg):
     assert check_bruteforce(cfg) < 1e-12
+
+
+@pytest.mark.parametrize("cfg", [TINY, TINY_GQA, TINY_LANES], ids=lambda c: c.name)
+def test_bruteforce_tiny_fp16_cache(cfg):
+    """the fp16-cache reading: K/V rounded to binary16 (struct 'e' format in
+    the brute force, numpy float16 in the oracle) before they are cached"""
+    assert check_bruteforce(cfg, kv_fp16=True) < 1e-12
+    # and the rounding really changes the result (so the option is live)
+    w = gen_weights(cfg, std=0.5, threads=1)
+    a = O.Oracle(cfg, w).run(gen_prompt(cfg), 2)["logits"][-1]
+    b = O.Oracle(cfg, w, kv_fp16=True).run(gen_prompt(cfg), 2)["logits"][-1]
+    assert 1e-7 < rel(a, b) < 1e-2
 
 
 @pytest.mark.parametrize("cfg", [TINY, TINY_GQA, TINY_LANES], ids=lambda c: c.name)
