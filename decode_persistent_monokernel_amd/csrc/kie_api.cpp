@@ -35,6 +35,8 @@ struct kie_ctx {
   uint64_t timeout_us = 2000000;
   uint32_t debug = 0;
   int32_t launch_steps = 512;
+  uint64_t* trace = nullptr;
+  int32_t trace_steps = 0;
   double clock_khz = 100000.0;
   std::string err;
 };
@@ -170,6 +172,8 @@ kie::KParams base_params(const kie_ctx* c) {
   kp.timeout_ticks = (uint64_t)((double)c->timeout_us * c->clock_khz / 1000.0);
   if (kp.timeout_ticks == 0) kp.timeout_ticks = 1;
   kp.debug_flags = c->debug;
+  kp.trace = c->trace;
+  kp.trace_steps = c->trace_steps;
   return kp;
 }
 
@@ -396,6 +400,13 @@ kie_status kie_set_timeout_us(kie_ctx* c, uint64_t us) {
 kie_status kie_set_debug_flags(kie_ctx* c, uint32_t flags) {
   if (!c) return KIE_ERR_INVALID_ARG;
   c->debug = flags;
+  return KIE_OK;
+}
+
+kie_status kie_set_trace(kie_ctx* c, void* d_trace, int32_t steps) {
+  if (!c || steps < 0 || (steps > 0 && !d_trace)) return KIE_ERR_INVALID_ARG;
+  c->trace = (uint64_t*)d_trace;
+  c->trace_steps = d_trace ? steps : 0;
   return KIE_OK;
 }
 

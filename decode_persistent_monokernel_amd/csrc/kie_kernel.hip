@@ -37,6 +37,8 @@ constexpr int kDepth = kRingDepth;  // 1-KB wave units in flight per wave (LDS r
 // operations are outstanding (expcnt and lgkmcnt left at their maximum)
 constexpr int kWaitRing = ((kDepth - 1) & 15) | (((kDepth - 1) >> 4) << 14) | (7 << 4) | (15 << 8);
 constexpr int kWaitAllVm = (7 << 4) | (15 << 8);
+// s_waitcnt immediate for lgkmcnt(0) only (vmcnt and expcnt at their maximum)
+constexpr int kWaitLgkm = 15 | (3 << 14) | (7 << 4);
 
 #define KIE_DI __device__ __forceinline__
 
@@ -118,6 +120,18 @@ KIE_DI void lse_merge(float& m, float& l, float* acc, float mo, float lo, const 
   m = mn;
 }
 
+// Workgroup barrier for LDS data.  __syncthreads() would also order this
+// wave's LDS-DMA ring loads (they write LDS) and so wait for every ring load
+// in flight; no other wave reads a wave's ring, so only this wave's ordinary
+// LDS accesses must be complete.  The empty asm statements keep the compiler
+// from moving memory accesses across the barrier.
+KIE_DI void wg_sync() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(kWaitLgkm);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // one key into an online softmax: (m, l, acc) += exp2(s - m) * v
 KIE_DI void online_update(float& m, float& l, float* acc, float s, const float* v) {
   const float mn = fmaxf(m, s);
@@ -183,32 +197,62 @@ KIE_DI bool spin_word(const Dev& D, const u64* a, uint32_t epoch, u64* out) {
   }
 }
 
-KIE_DI float poll_f(const Dev& D, const u64* a, uint32_t epoch) {
-  u64 w = ll_load(a);
-  if (ll_epoch(w) != epoch) spin_word(D, a, epoch, &w);
-  return ll_f(w);
+// phase trace stamp (thread 0 of the workgroup only)
+KIE_DI void stamp(const Dev& D, int s, int ph, int k) {
+  const KParams& p = *D.p;
+  if (p.trace && s < p.trace_steps && D.tid == 0)
+    p.trace[(((uint64_t)s * kTracePhases + ph) * D.nwg + D.wg) * 4 + k] = wall_clock64();
+}
+
+// Wait until the words base[k*stride] (k < N, mask bit k set) all carry
+// `epoch`.  Every round re-issues the loads of all words still stale
+// together, so detection costs one memory round trip after the last word
+// lands rather than one per word.  Returns false on timeout or abort.
+template <int N>
+KIE_DI bool poll_words(const Dev& D, const u64* base, int stride, uint32_t mask, uint32_t epoch, u64 (&v)[N]) {
+#pragma unroll
+  for (int k = 0; k < N; ++k)
+    if (mask & (1u << k)) v[k] = ll_load(base + (long)k * stride);
+  uint64_t t0 = 0;
+  for (int it = 0;; ++it) {
+    uint32_t stale = 0;
+#pragma unroll
+    for (int k = 0; k < N; ++k)
+      if ((mask & (1u << k)) && ll_epoch(v[k]) != epoch) stale |= 1u << k;
+    if (!stale) return true;
+    if (it == 0) t0 = wall_clock64();
+    if ((it & 15) == 15) {
+      if (*(volatile int*)&D.sh->abort) return false;
+      if (__hip_atomic_load(&D.state[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+        D.sh->abort = 1;
+        return false;
+      }
+      if (wall_clock64() - t0 > D.p->timeout_ticks) {
+        raise_status(D, DEV_TIMEOUT);
+        return false;
+      }
+    }
+    __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+    for (int k = 0; k < N; ++k)
+      if (stale & (1u << k)) v[k] = ll_load(base + (long)k * stride);
+  }
 }
 
 // the workgroup polls words [0, n) of src into dst (swizzled for GEMV input)
 template <bool SWZ>
 KIE_DI void poll_to_lds(const Dev& D, const u64* src, float* dst, int n, uint32_t epoch) {
   for (int base = D.tid; base < n; base += kThreads * 8) {
+    uint32_t mask = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (base + k * kThreads < n) mask |= 1u << k;
     u64 v[8];
+    if (!poll_words<8>(D, src + base, kThreads, mask, epoch, v)) return;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const int i = base + k * kThreads;
-      v[k] = 0;
-      if (i < n) v[k] = ll_load(src + i);
-    }
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int i = base + k * kThreads;
-      if (i < n) {
-        if (ll_epoch(v[k]) != epoch) {
-          if (!spin_word(D, src + i, epoch, &v[k])) return;
-        }
-        dst[SWZ ? xs_pos(i) : i] = ll_f(v[k]);
-      }
+      if (i < n) dst[SWZ ? xs_pos(i) : i] = ll_f(v[k]);
     }
   }
 }
@@ -381,28 +425,62 @@ KIE_DI void cursor_issue(const Dev& D, Cursor& c, int slot) {
                                    16, 0, 2 /* nt */);
 }
 
-// read this lane's 16 bytes of a ring slot.  The read is written as asm and
-// waits for itself, so the compiler neither sees an LDS access that the ring
-// DMAs could alias nor leaves an output register in flight.
+// read this lane's 16 bytes of ring slots.  The reads are written as asm and
+// wait for themselves, so the compiler neither sees an LDS access that the
+// ring DMAs could alias nor leaves an output register in flight.
+KIE_DI uint32_t ring_addr(const Dev& D, int slot) {
+  return (uint32_t)(uintptr_t)(D.ring + slot * kWave + D.lane);
+}
 KIE_DI uint4 ring_read(const Dev& D, int slot) {
   uint4 x;
-  const uint32_t addr = (uint32_t)(uintptr_t)(D.ring + slot * kWave + D.lane);
-  asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(x) : "v"(addr) : "memory");
+  asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(x) : "v"(ring_addr(D, slot)) : "memory");
   return x;
 }
+KIE_DI void ring_read4(const Dev& D, int s0, int s1, int s2, int s3, uint4& x0, uint4& x1, uint4& x2, uint4& x3) {
+  asm volatile(
+      "ds_read_b128 %0, %4\n\t"
+      "ds_read_b128 %1, %5\n\t"
+      "ds_read_b128 %2, %6\n\t"
+      "ds_read_b128 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(x0), "=&v"(x1), "=&v"(x2), "=&v"(x3)
+      : "v"(ring_addr(D, s0)), "v"(ring_addr(D, s1)), "v"(ring_addr(D, s2)), "v"(ring_addr(D, s3))
+      : "memory");
+}
+
+KIE_DI int ring_next(int s) { return s + 1 == kDepth ? 0 : s + 1; }
 
 // ---------------------------------------------------------------------------
 // the ring: consume the next n units.  Exactly one DMA is issued per unit
-// consumed, so when unit c is read the kDepth-1 younger DMAs may stay in flight
-// (vector memory reads complete in order).
+// consumed, so when units c..c+3 are read the kDepth-4 younger DMAs may stay
+// in flight (vector memory reads complete in order).  Units are taken four at
+// a time so that one LDS round trip serves four of them.
 // ---------------------------------------------------------------------------
+constexpr int kWaitRing4 = ((kDepth - 4) & 15) | (((kDepth - 4) >> 4) << 14) | (7 << 4) | (15 << 8);
+
 template <class F>
 KIE_DI void run_units(const Dev& D, Cursor& cur, int& slot, int n, F& consume) {
-  for (int j = 0; j < n; ++j) {
+  int j = 0;
+  for (; j + 4 <= n; j += 4) {
+    __builtin_amdgcn_s_waitcnt(kWaitRing4);
+    const int s0 = slot, s1 = ring_next(s0), s2 = ring_next(s1), s3 = ring_next(s2);
+    uint4 x0, x1, x2, x3;
+    ring_read4(D, s0, s1, s2, s3, x0, x1, x2, x3);
+    cursor_issue(D, cur, s0);
+    cursor_issue(D, cur, s1);
+    cursor_issue(D, cur, s2);
+    cursor_issue(D, cur, s3);
+    slot = ring_next(s3);
+    consume(x0, j, false);
+    consume(x1, j + 1, false);
+    consume(x2, j + 2, false);
+    consume(x3, j + 3, j + 3 == n - 1);
+  }
+  for (; j < n; ++j) {
     __builtin_amdgcn_s_waitcnt(kWaitRing);
     const uint4 x = ring_read(D, slot);
     cursor_issue(D, cur, slot);
-    slot = slot + 1 == kDepth ? 0 : slot + 1;
+    slot = ring_next(slot);
     consume(x, j, j == n - 1);
   }
 }
@@ -418,7 +496,7 @@ KIE_DI void rmsnorm_to_xs(const Dev& D, const float* xraw, const uint16_t* g, fl
   for (int i = D.tid; i < d; i += kThreads) ss += xraw[i] * xraw[i];
   ss = wave_sum(ss);
   if (D.lane == 0) D.sh->redf[D.wave] = ss;
-  __syncthreads();
+  wg_sync();
   float tot = 0.f;
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) tot += D.sh->redf[w];
@@ -567,7 +645,7 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
       }
     }
   }
-  __syncthreads();
+  wg_sync();
 
   // cursor and ring (started at the top of every step)
   Cursor cur;
@@ -622,11 +700,11 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
       const uint16_t* e = p.W + p.pl.embed + (uint64_t)token * d;
       for (int i = D.tid; i < d; i += kThreads) xraw[i] = hbits2f(e[i]);
     }
-    __syncthreads();
+    wg_sync();
     if (p.m.parallel) {
       const int r0 = wgrows[2 * 3], nr = wgrows[2 * 3 + 1];
       for (int t = D.tid; t < nr; t += kThreads) own[nr + t] = xraw[r0 + t];
-      __syncthreads();
+      wg_sync();
     }
 
     if ((p.debug_flags & DBG_WAIT_NEVER) && D.wg == 0) {
@@ -635,7 +713,7 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
         u64 dummy;
         spin_word(D, D.LMP + 2 * D.nwg - 1, 0xFFFFFFFFu, &dummy);
       }
-      __syncthreads();
+      wg_sync();
       if (D.sh->abort) { __builtin_amdgcn_s_waitcnt(kWaitAllVm); return; }
     }
 
@@ -646,6 +724,7 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
       const int l = is_lm ? L : ph / 5;
       const uint16_t* Wl = p.W + (uint64_t)(is_lm ? 0 : l) * p.pl.layer_stride;
 
+      stamp(D, s, ph, 0);
       if (kind == PH_ATTN) {
         // ================= attention over the KV cache ==================
         float mrow[G], lrow[G], acc[G][8], q[G][8], sc[G];
@@ -665,18 +744,13 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
           // this lane's 8 query dims of every head in the group
           {
             const u64* qb = D.Q + (uint64_t)l * qd + (uint64_t)g * G * hd + D.dl * 8;
-            u64 qw[G][8];
 #pragma unroll
-            for (int h = 0; h < G; ++h)
+            for (int h = 0; h < G; ++h) {
+              u64 qw[8];
+              poll_words<8>(D, qb + h * hd, 1, 0xFFu, epoch, qw);
 #pragma unroll
-              for (int e = 0; e < 8; ++e) qw[h][e] = ll_load(qb + h * hd + e);
-#pragma unroll
-            for (int h = 0; h < G; ++h)
-#pragma unroll
-              for (int e = 0; e < 8; ++e) {
-                if (ll_epoch(qw[h][e]) != epoch) spin_word(D, qb + h * hd + e, epoch, &qw[h][e]);
-                q[h][e] = ll_f(qw[h][e]);
-              }
+              for (int e = 0; e < 8; ++e) q[h][e] = ll_f(qw[e]);
+            }
           }
           AttnConsume<G> ac{mrow, lrow, acc, q, sc, ka, kc, D.kpl, D.kl, D.lpk, D.lane_active};
           run_units(D, cur, slot, 2 * nst, ac);
@@ -686,15 +760,10 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
             const u64* vp = D.VC + (uint64_t)l * kvd + (uint64_t)g * hd + D.dl * 8;
             u64 kw[8], vw[8];
             float kx[8], vx[8];
+            poll_words<8>(D, kp, 1, 0xFFu, epoch, kw);
+            poll_words<8>(D, vp, 1, 0xFFu, epoch, vw);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-              kw[e] = ll_load(kp + e);
-              vw[e] = ll_load(vp + e);
-            }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              if (ll_epoch(kw[e]) != epoch) spin_word(D, kp + e, epoch, &kw[e]);
-              if (ll_epoch(vw[e]) != epoch) spin_word(D, vp + e, epoch, &vw[e]);
               kx[e] = ll_f(kw[e]);
               vx[e] = ll_f(vw[e]);
             }
@@ -737,7 +806,8 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
             }
           }
         }
-        __syncthreads();
+        stamp(D, s, ph, 1);
+        wg_sync();
         if (D.sh->abort) { __builtin_amdgcn_s_waitcnt(kWaitAllVm); return; }
         // workgroup merge of the waves -> one record per segment
         for (int sg = 0; sg < nseg; ++sg) {
@@ -760,6 +830,7 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
             ll_storef(rec + h * (hd + 2) + 2 + dd, O, epoch);
           }
         }
+        stamp(D, s, ph, 2);
         // merger: the workgroup holding head g's last key combines the
         // records of every workgroup that met head g
         const int merge_g = adesc[11];
@@ -768,75 +839,98 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
           const int n_ctx = pos + 1;
           const int w_first = attn_owner(Hkv, n_ctx, D.nwg, g, 0);
           const int nrec = D.wg - w_first + 1;
-          // mlw[(r*G + h)*4 + {0: m, 1: l, 2: weight, 3: segment or -1}]
-          for (int t = D.tid; t < nrec * G; t += kThreads) {
-            const int r = t / G, h = t % G;
+          // 1. which records exist: mlw[r*4 + 3] = segment of record r or -1
+          for (int r = D.tid; r < nrec; r += kThreads) {
             AttnSeg sgs[2];
             sgs[0] = AttnSeg{0, 0, 0};
             sgs[1] = AttnSeg{0, 0, 0};
             const int ns = attn_segments(Hkv, n_ctx, D.nwg, w_first + r, sgs);
-            float m = -INFINITY, lsum = 0.f, segi = -1.f;
-            if (ns > 0) {
-              const int si = (sgs[0].g == g) ? 0 : 1;
-              const u64* rec = D.REC + (((uint64_t)l * D.nwg + w_first + r) * 2 + si) * G * (hd + 2) + h * (hd + 2);
-              m = poll_f(D, rec, epoch);
-              lsum = poll_f(D, rec + 1, epoch);
-              segi = (float)si;
-            }
-            mlw[t * 4 + 0] = m;
-            mlw[t * 4 + 1] = lsum;
-            mlw[t * 4 + 3] = segi;
+            mlw[r * 4 + 3] = ns > 0 ? (float)((sgs[0].g == g) ? 0 : 1) : -1.f;
           }
-          __syncthreads();
+          wg_sync();
+          // 2. one poll round: every word of every record into LDS
+          //    (record r, head h at recs[(r*G + h)*(hd+2) ...])
+          float* recs = wrec;  // the wave records are consumed already
+          const int rw = G * (hd + 2);
+          for (int base = D.tid; base < nrec * rw; base += kThreads * 8) {
+            u64 vv[8];
+            uint32_t mask = 0;
+            const u64* addr[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+              const int i = base + k * kThreads;
+              addr[k] = D.REC;
+              if (i < nrec * rw) {
+                const int r = i / rw, off = i % rw;
+                const int si = (int)mlw[r * 4 + 3];
+                if (si >= 0) {
+                  addr[k] = D.REC + (((uint64_t)l * D.nwg + w_first + r) * 2 + si) * rw + off;
+                  mask |= 1u << k;
+                }
+              }
+            }
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+              if (mask & (1u << k)) vv[k] = ll_load(addr[k]);
+            const uint64_t t0 = wall_clock64();
+            for (int it = 0;; ++it) {
+              uint32_t stale = 0;
+#pragma unroll
+              for (int k = 0; k < 8; ++k)
+                if ((mask & (1u << k)) && ll_epoch(vv[k]) != epoch) stale |= 1u << k;
+              if (!stale) break;
+              if ((it & 15) == 15) {
+                if (*(volatile int*)&D.sh->abort) break;
+                if (__hip_atomic_load(&D.state[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+                  D.sh->abort = 1;
+                  break;
+                }
+                if (wall_clock64() - t0 > D.p->timeout_ticks) {
+                  raise_status(D, DEV_TIMEOUT);
+                  break;
+                }
+              }
+              __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+              for (int k = 0; k < 8; ++k)
+                if (stale & (1u << k)) vv[k] = ll_load(addr[k]);
+            }
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+              const int i = base + k * kThreads;
+              if (i < nrec * rw) {
+                const int off = i % rw;
+                float v = 0.f;
+                if (mask & (1u << k)) {
+                  v = ll_f(vv[k]);
+                } else if (off % (hd + 2) == 0) {
+                  v = -INFINITY;  // missing record: empty
+                }
+                recs[i] = v;
+              }
+            }
+          }
+          wg_sync();
           if (D.sh->abort) { __builtin_amdgcn_s_waitcnt(kWaitAllVm); return; }
-          for (int t = D.tid; t < nrec * G; t += kThreads) {
-            const int h = t % G;
-            float M = -INFINITY;
-            for (int r = 0; r < nrec; ++r) M = fmaxf(M, mlw[(r * G + h) * 4]);
-            float Ls = 0.f;
-            for (int r = 0; r < nrec; ++r) {
-              const float m = mlw[(r * G + h) * 4];
-              Ls += (m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - M)) * mlw[(r * G + h) * 4 + 1];
-            }
-            const float m = mlw[t * 4];
-            mlw[t * 4 + 2] = (m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - M)) / Ls;
-          }
-          __syncthreads();
+          // 3. combine: o = sum_r exp2(m_r - M) O_r / sum_r exp2(m_r - M) l_r
           for (int t = D.tid; t < G * hd; t += kThreads) {
             const int h = t / hd, dd = t % hd;
-            float o = 0.f;
-            for (int rb = 0; rb < nrec; rb += 8) {
-              u64 vv[8];
-#pragma unroll
-              for (int k = 0; k < 8; ++k) {
-                const int r = rb + k;
-                vv[k] = 0;
-                if (r < nrec && mlw[(r * G + h) * 4 + 3] >= 0.f) {
-                  const int si = (int)mlw[(r * G + h) * 4 + 3];
-                  vv[k] = ll_load(D.REC + (((uint64_t)l * D.nwg + w_first + r) * 2 + si) * G * (hd + 2) +
-                                  h * (hd + 2) + 2 + dd);
-                }
-              }
-#pragma unroll
-              for (int k = 0; k < 8; ++k) {
-                const int r = rb + k;
-                if (r < nrec && mlw[(r * G + h) * 4 + 3] >= 0.f) {
-                  if (ll_epoch(vv[k]) != epoch) {
-                    const int si = (int)mlw[(r * G + h) * 4 + 3];
-                    spin_word(D,
-                              D.REC + (((uint64_t)l * D.nwg + w_first + r) * 2 + si) * G * (hd + 2) +
-                                  h * (hd + 2) + 2 + dd,
-                              epoch, &vv[k]);
-                  }
-                  o += mlw[(r * G + h) * 4 + 2] * ll_f(vv[k]);
-                }
-              }
+            float M = -INFINITY;
+            for (int r = 0; r < nrec; ++r) M = fmaxf(M, recs[(r * G + h) * (hd + 2)]);
+            float Ls = 0.f, o = 0.f;
+            for (int r = 0; r < nrec; ++r) {
+              const float* rr = recs + (r * G + h) * (hd + 2);
+              const float a = rr[0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(rr[0] - M);
+              Ls += a * rr[1];
+              o += a * rr[2 + dd];
             }
+            o = o / Ls;
             ll_storef(D.OB + (uint64_t)l * qd + (uint64_t)(g * G + h) * hd + dd, o, epoch);
           }
         }
-        __syncthreads();
+        wg_sync();
         if (D.sh->abort) { __builtin_amdgcn_s_waitcnt(kWaitAllVm); return; }
+        stamp(D, s, ph, 3);
         continue;
       }
 
@@ -848,14 +942,14 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
         if (p.m.parallel ? (l > p.m.delay) : (l > 0)) {
           const int xi = p.m.parallel ? l : 2 * l;
           poll_to_lds<false>(D, D.X + (uint64_t)xi * d, xraw, d, epoch);
-          __syncthreads();
+          wg_sync();
           if (D.sh->abort) { __builtin_amdgcn_s_waitcnt(kWaitAllVm); return; }
         }
         rmsnorm_to_xs(D, xraw, Wl + p.pl.attn_norm, xs);
       } else if (kind == PH_GU) {
         if (!p.m.parallel) {
           poll_to_lds<false>(D, D.X + (uint64_t)(2 * l + 1) * d, xraw, d, epoch);
-          __syncthreads();
+          wg_sync();
           if (D.sh->abort) { __builtin_amdgcn_s_waitcnt(kWaitAllVm); return; }
         }
         rmsnorm_to_xs(D, xraw, Wl + p.pl.mlp_norm, xs);
@@ -867,20 +961,22 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
         zero_tail(D, xs, F);
       } else {  // LM
         poll_to_lds<false>(D, D.X + (uint64_t)(2 * L) * d, xraw, d, epoch);
-        __syncthreads();
+        wg_sync();
         if (D.sh->abort) { __builtin_amdgcn_s_waitcnt(kWaitAllVm); return; }
         rmsnorm_to_xs(D, xraw, p.W + p.pl.final_norm, xs);
       }
       for (int i = D.tid; i < nrows * kWaves; i += kThreads) part[i] = 0.f;
-      __syncthreads();
+      wg_sync();
       if (D.sh->abort) { __builtin_amdgcn_s_waitcnt(kWaitAllVm); return; }
+      stamp(D, s, ph, 1);
 
       {
         const int* gd = D.desc + D.wave * kWaveDesc + 8 * gi;
         GemvConsume c{(const float4*)xs, part, gd[6], gd[2], gd[4], D.lane, D.wave, 0.f};
         run_units(D, cur, slot, gd[3], c);
       }
-      __syncthreads();
+      stamp(D, s, ph, 2);
+      wg_sync();
 
       // epilogue
       if (kind == PH_QKV) {
@@ -997,14 +1093,20 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
           D.sh->lmi[D.wave] = my_idx;
         }
       }
-      __syncthreads();
+      wg_sync();
+      stamp(D, s, ph, 3);
     }  // phases
 
     // ---- end of step: release the KV writes, publish, gather ------------
+    const int tph = 5 * 64 + 1;
+    stamp(D, s, tph, 0);
     const bool lm = lm_active(p, s);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    __syncthreads();
+    // every thread's KV-cache stores have reached the L2 before thread 0's
+    // release fence writes the L2 back (one write-back per workgroup)
+    __builtin_amdgcn_s_waitcnt(kWaitAllVm);
+    wg_sync();
     if (D.tid == 0) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
       float bv = -INFINITY;
       int bi = 0x7FFFFFFF;
       if (lm) {
@@ -1026,15 +1128,21 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
     float* lv = xs;
     int* li = (int*)(xs + D.nwg);
     for (int t = D.tid; t < D.nwg; t += kThreads) {
-      u64 a = ll_load(D.LMP + 2 * t), b = ll_load(D.LMP + 2 * t + 1);
-      if (ll_epoch(a) != epoch) spin_word(D, D.LMP + 2 * t, epoch, &a);
-      if (ll_epoch(b) != epoch) spin_word(D, D.LMP + 2 * t + 1, epoch, &b);
-      lv[t] = ll_f(a);
-      li[t] = (int)(uint32_t)b;
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      u64 ab[2];
+      poll_words<2>(D, D.LMP + 2 * t, 1, 3u, epoch, ab);
+      lv[t] = ll_f(ab[0]);
+      li[t] = (int)(uint32_t)ab[1];
     }
-    __syncthreads();
+    wg_sync();
+    // every workgroup's release is now observed: one acquire (L1 and L2
+    // invalidate) before this workgroup reads KV rows of the next step
+    if (D.tid == 0) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      __builtin_amdgcn_s_waitcnt(kWaitAllVm);
+    }
+    wg_sync();
     if (D.sh->abort) { __builtin_amdgcn_s_waitcnt(kWaitAllVm); return; }
+    stamp(D, s, tph, 1);
     if (lm) {
       if (D.tid == 0) {
         float bv = lv[0];
@@ -1047,14 +1155,14 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
         }
         D.sh->token = bi;
       }
-      __syncthreads();
+      wg_sync();
       token = D.sh->token;
       if (D.wg == 0 && D.tid == 0) {
         if (p.out) p.out[p.lm_mode == 1 ? 0 : s] = token;
         D.state[2] = token;
       }
     }
-    __syncthreads();
+    wg_sync();
   }  // steps
   __builtin_amdgcn_s_waitcnt(kWaitAllVm);  // no ring DMA may outlive the workgroup
 }

@@ -235,7 +235,10 @@ constexpr int kDescInts = kWaves * kWaveDesc + 16;
 // whose LdsPlan needs more is rejected by the host (the ring adds
 // kWaves x kRingDepth KB)
 constexpr int kMainFloats = 23552;
-constexpr int kRingDepth = 8;
+#ifndef KIE_RING_DEPTH
+#define KIE_RING_DEPTH 8
+#endif
+constexpr int kRingDepth = KIE_RING_DEPTH;
 
 // LDS plan (in floats)
 struct LdsPlan {
@@ -266,9 +269,13 @@ KIE_HD LdsPlan lds_plan(const Dims& m, int nwg) {
   p.gemv_xs = o;
   p.gemv_part = o + kmax;
   const int gemv_sz = kmax + (int)align_up((uint64_t)rmax * kWaves, 64);
+  // attention: per-wave records (2 segments x kWaves), later reused by the
+  // merger for the records of every workgroup that met its head, then
+  // 4 floats per record
+  const int wrec_sz = imax(2 * kWaves * m.G * (m.hd + 2), max_recs * m.G * (m.hd + 2));
   p.attn_wrec = o;
-  p.attn_ml = o + 2 * kWaves * m.G * (m.hd + 2);
-  const int attn_sz = 2 * kWaves * m.G * (m.hd + 2) + max_recs * m.G * 4;
+  p.attn_ml = o + wrec_sz;
+  const int attn_sz = wrec_sz + max_recs * 4;
   o += (int)align_up((uint64_t)imax(gemv_sz, attn_sz), 64);
   p.own = o; o += (int)align_up((uint64_t)2 * ((m.d + nwg - 1) / nwg), 64);
   p.desc = o; o += kDescInts;
@@ -294,7 +301,13 @@ struct KParams {
   uint32_t epoch0;        // epoch of step 0
   uint64_t timeout_ticks; // wall-clock ticks a single wait may take
   uint32_t debug_flags;
+  // optional phase trace: for steps < trace_steps, workgroup wg's thread 0
+  // writes 4 wall-clock stamps per phase (start, input ready, stream done,
+  // end) at trace[((step * kTracePhases + phase) * nwg + wg) * 4]
+  uint64_t* trace;
+  int trace_steps;
 };
+constexpr int kTracePhases = 5 * 64 + 2;  // up to 64 layers, LM, step end
 
 enum DebugFlags : uint32_t {
   DBG_WAIT_NEVER = 1u,  // workgroup 0 waits on a word no one writes (timeout test)

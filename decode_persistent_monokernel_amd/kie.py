@@ -69,6 +69,7 @@ def lib() -> C.CDLL:
         L.kie_set_timeout_us.argtypes = [vp, C.c_uint64]
         L.kie_set_debug_flags.argtypes = [vp, C.c_uint32]
         L.kie_set_launch_steps.argtypes = [vp, i32]
+        L.kie_set_trace.argtypes = [vp, vp, i32]
         L.kie_pack_weights_host.argtypes = [C.POINTER(ModelConfigC), C.POINTER(WeightsC), vp]
         L.kie_launch_info.argtypes = [vp, C.POINTER(i32), C.POINTER(i32), C.POINTER(i32),
                                       C.POINTER(C.c_int64), C.POINTER(C.c_int64)]
@@ -83,7 +84,7 @@ def lib() -> C.CDLL:
         L.kie_destroy.restype = None
         for name in ("kie_create", "kie_query_sizes", "kie_bind_memory", "kie_load_weights",
                      "kie_prefill", "kie_decode", "kie_set_position", "kie_sync_status",
-                     "kie_set_timeout_us", "kie_set_debug_flags", "kie_set_launch_steps",
+                     "kie_set_timeout_us", "kie_set_debug_flags", "kie_set_launch_steps", "kie_set_trace",
                      "kie_pack_weights_host", "kie_launch_info", "kie_validate_schedule"):
             getattr(L, name).restype = C.c_int
         _lib = L
@@ -224,6 +225,25 @@ class Engine:
 
     def set_debug_flags(self, flags: int):
         _check(self.L.kie_set_debug_flags(self.ctx, int(flags)), self.ctx)
+
+    TRACE_PHASES = 5 * 64 + 2
+
+    def set_trace(self, steps: int):
+        """allocate a trace buffer for the first `steps` steps of each launch
+        (0 turns tracing off); read it back with trace()"""
+        t = self.torch
+        if steps <= 0:
+            self._trace = None
+            _check(self.L.kie_set_trace(self.ctx, None, 0), self.ctx)
+            return
+        nwg = self.launch_info()["n_workgroups"]
+        self._trace = t.zeros(steps * self.TRACE_PHASES * nwg * 4, dtype=t.int64, device=self.dev)
+        self._trace_shape = (steps, self.TRACE_PHASES, nwg, 4)
+        _check(self.L.kie_set_trace(self.ctx, self._trace.data_ptr(), steps), self.ctx)
+
+    def trace(self) -> np.ndarray:
+        """[steps, phases, workgroups, 4] wall-clock stamps (100 MHz ticks)"""
+        return self._trace.cpu().numpy().reshape(self._trace_shape)
 
     def set_launch_steps(self, n: int):
         _check(self.L.kie_set_launch_steps(self.ctx, int(n)), self.ctx)

@@ -159,6 +159,14 @@ kie_status kie_set_timeout_us(kie_ctx* ctx, uint64_t microseconds);
  * must end in KIE_ERR_TIMEOUT, not a hang).  0 = normal operation. */
 kie_status kie_set_debug_flags(kie_ctx* ctx, uint32_t flags);
 
+/* Phase trace for performance analysis.  When d_trace is not NULL, the
+ * first `steps` steps of every launch write, per phase and workgroup, four
+ * 64-bit wall-clock stamps (phase start, input ready, stream done, phase end)
+ * into device memory d_trace at index ((step*322 + phase)*n_workgroups + wg)*4
+ * (phase 321 is the end-of-step exchange).  The caller owns the buffer
+ * (steps*322*n_workgroups*32 bytes).  NULL / 0 turns tracing off. */
+kie_status kie_set_trace(kie_ctx* ctx, void* d_trace, int32_t steps);
+
 /* Most decode steps one launch runs before the library starts the next one
  * (default 512); keeps each launch short. */
 kie_status kie_set_launch_steps(kie_ctx* ctx, int32_t steps);

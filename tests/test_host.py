@@ -164,8 +164,8 @@ def test_schedule_covers_everything(cfg):
             try:
                 kie.validate_schedule(cfg, nwg, n)
             except kie.KieError as e:
-                # fewer workgroups can leave too many LM-head rows for the LDS plan
-                assert nwg < 256 and "LDS" in str(e), str(e)
+                # other workgroup counts can overflow the LDS plan (MI355X has 256 CUs)
+                assert nwg != 256 and "LDS" in str(e), str(e)
 
 
 @needs_lib
