@@ -89,6 +89,7 @@ kie::Dims make_dims(const kie_model_config& c) {
 std::string check_supported(const kie::Dims& m, int nwg) {
   if (m.G != 1 && m.G != 2 && m.G != 4) return "query heads per KV head must be 1, 2 or 4";
   if (m.hd / 8 > 64) return "head_dim above 512 is not supported";
+  if (m.d > kie::kGainRegs * kie::kThreads) return "d_model above 4096 is not supported";
   if (m.Hkv > nwg) return "more KV heads than workgroups";
   const kie::LdsPlan lp = kie::lds_plan(m, nwg);
   if (lp.total_floats > kie::kMainFloats) return "model needs more LDS than the kernel reserves";
@@ -105,6 +106,13 @@ std::string check_supported(const kie::Dims& m, int nwg) {
 // ---------------------------------------------------------------------------
 void copy_rows(uint16_t* dst, const uint16_t* src, size_t n) { std::memcpy(dst, src, n * sizeof(uint16_t)); }
 
+// n rows of k elements from src (stride k) to dst (stride row_stride(k))
+void copy_matrix(uint16_t* dst, const uint16_t* src, size_t n, int k) {
+  const size_t rs = kie::row_stride(k);
+  if (rs == (size_t)k) return copy_rows(dst, src, n * k);
+  for (size_t r = 0; r < n; ++r) copy_rows(dst + r * rs, src + r * k, k);
+}
+
 bool weights_complete(const kie_model_config& c, const kie_weights* w) {
   if (!w || !w->embed || !w->lm_head || !w->final_norm || !w->attn_norm || !w->wq || !w->wk || !w->wv || !w->wo ||
       !w->mlp_norm || !w->w_gate || !w->w_up || !w->w_down)
@@ -119,6 +127,7 @@ bool weights_complete(const kie_model_config& c, const kie_weights* w) {
 // pack layer l into dst (layer_stride elements)
 void pack_layer(const kie::Dims& m, const kie::PackLayout& pl, const kie_weights* w, int l, uint16_t* dst) {
   const size_t d = m.d, qd = (size_t)m.H * m.hd, F = m.F;
+  const size_t sd = kie::row_stride(m.d);
   std::memset(dst, 0, pl.layer_stride * sizeof(uint16_t));
   copy_rows(dst + pl.attn_norm, w->attn_norm[l], d);
   const int rows = (m.H + 2 * m.Hkv) * m.hd;
@@ -126,15 +135,15 @@ void pack_layer(const kie::Dims& m, const kie::PackLayout& pl, const kie_weights
     int which, src;
     kie::qkv_source_row(m, r, &which, &src);
     const uint16_t* s = which == 0 ? w->wq[l] : which == 1 ? w->wk[l] : w->wv[l];
-    copy_rows(dst + pl.wqkv + (size_t)r * d, s + (size_t)src * d, d);
+    copy_rows(dst + pl.wqkv + (size_t)r * sd, s + (size_t)src * d, d);
   }
-  copy_rows(dst + pl.wo, w->wo[l], d * qd);
+  copy_matrix(dst + pl.wo, w->wo[l], d, (int)qd);
   copy_rows(dst + pl.mlp_norm, w->mlp_norm[l], d);
   for (size_t f = 0; f < F; ++f) {
-    copy_rows(dst + pl.wgu + (2 * f) * d, w->w_gate[l] + f * d, d);
-    copy_rows(dst + pl.wgu + (2 * f + 1) * d, w->w_up[l] + f * d, d);
+    copy_rows(dst + pl.wgu + (2 * f) * sd, w->w_gate[l] + f * d, d);
+    copy_rows(dst + pl.wgu + (2 * f + 1) * sd, w->w_up[l] + f * d, d);
   }
-  copy_rows(dst + pl.wd, w->w_down[l], d * F);
+  copy_matrix(dst + pl.wd, w->w_down[l], d, (int)F);
 }
 
 // the part after the layers: final_norm, lm_head, embed
@@ -142,7 +151,7 @@ void pack_tail(const kie::Dims& m, const kie::PackLayout& pl, const kie_weights*
   const uint64_t base = pl.final_norm;
   std::memset(dst_at_final_norm, 0, (pl.total - base) * sizeof(uint16_t));
   copy_rows(dst_at_final_norm + (pl.final_norm - base), w->final_norm, m.d);
-  copy_rows(dst_at_final_norm + (pl.lm_head - base), w->lm_head, (size_t)m.V * m.d);
+  copy_matrix(dst_at_final_norm + (pl.lm_head - base), w->lm_head, (size_t)m.V, m.d);
   copy_rows(dst_at_final_norm + (pl.embed - base), w->embed, (size_t)m.V * m.d);
 }
 
@@ -253,7 +262,7 @@ kie_status kie_create(const kie_model_config* cfg, int device, kie_ctx** out) {
 kie_status kie_query_sizes(const kie_ctx* c, size_t* packed, size_t* kv, size_t* ws) {
   if (!c) return KIE_ERR_INVALID_ARG;
   if (packed) *packed = (size_t)c->pl.total * 2;
-  if (kv) *kv = (size_t)kie::kv_elems(c->m) * 2;
+  if (kv) *kv = (size_t)kie::kv_alloc_elems(c->m) * 2;
   if (ws) *ws = (size_t)c->wl.total;
   return KIE_OK;
 }
@@ -387,6 +396,12 @@ kie_status kie_sync_status(kie_ctx* c, void* stream) {
   const int32_t zero[2] = {0, 0};
   e = hipMemcpy((uint8_t*)c->ws + c->wl.state, zero, sizeof(zero), hipMemcpyHostToDevice);
   if (e != hipSuccess) return hip_fail(c, e, "clear status");
+  // an aborted launch leaves exchange words and arrival counters part-way
+  // through a step: start the exchange state over (the KV cache is kept)
+  e = kie_internal_zero((uint8_t*)c->ws + c->wl.ll_begin, c->wl.ll_end - c->wl.ll_begin, nullptr);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) return hip_fail(c, e, "reset exchange state");
+  c->next_epoch = 1;
   if (st[0] == kie::DEV_BAD_TOKEN) return fail(c, KIE_ERR_BAD_TOKEN, "a token id outside [0, vocab) reached the kernel");
   return fail(c, KIE_ERR_TIMEOUT, "a wait inside the decode kernel timed out");
 }
@@ -463,19 +478,22 @@ kie_status kie_validate_schedule(const kie_model_config* cfg, int32_t nwg, int32
         if (r < 0 || r >= sh.rows || owner[r] != -1) return bad("GEMV row owned twice or out of range");
         owner[r] = w;
       }
-      const int nb = kie::blocks_per_row(sh.K);
-      std::vector<int> seen((size_t)(r1 - r0) * nb, 0);
+      // chunks of the workgroup's packed stretch: contiguous per wave, every
+      // packed element of its rows read by exactly one wave
+      const int rs = kie::row_stride(sh.K);
+      const int nch = kie::gemv_chunks(r1 - r0, sh.K);
+      const int64_t elems = (int64_t)(r1 - r0) * rs;
+      if ((int64_t)nch * kie::kBlock < elems || (nch > 0 && (int64_t)(nch - 1) * kie::kBlock >= elems))
+        return bad("chunk count does not match the workgroup rows");
+      if (rs < kie::kBlock) return bad("row stride below one chunk");
       int prev_end = 0;
       for (int wave = 0; wave < kie::kWaves; ++wave) {
-        int u0, u1;
-        kie::gemv_wave_units(r1 - r0, sh.K, wave, &u0, &u1);
-        if (u0 != prev_end || u1 < u0) return bad("wave unit ranges not contiguous");
-        prev_end = u1;
-        for (int u = u0; u < u1; ++u) seen[u]++;
+        int c0, c1;
+        kie::gemv_wave_chunks(r1 - r0, sh.K, wave, &c0, &c1);
+        if (c0 != prev_end || c1 < c0) return bad("wave chunk ranges not contiguous");
+        prev_end = c1;
       }
-      if (prev_end != (r1 - r0) * nb) return bad("wave units do not cover the workgroup rows");
-      for (int v : seen)
-        if (v != 1) return bad("GEMV unit covered twice");
+      if (prev_end != nch) return bad("wave chunks do not cover the workgroup rows");
     }
     for (int r = 0; r < sh.rows; ++r)
       if (owner[r] < 0) return bad("GEMV row not owned");

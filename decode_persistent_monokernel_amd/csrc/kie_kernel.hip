@@ -13,9 +13,11 @@
 //  * one workgroup per compute unit (grid = CU count, co-resident by
 //    cooperative launch), 8 wave64s per workgroup;
 //  * every wave streams its slice of the weights (and, for attention, of the
-//    KV cache) through a ring of kDepth 16-byte-per-lane registers; the load
-//    cursor runs ahead of the consumer across phase boundaries, so weight
-//    bytes keep flowing while a wave waits for the activation it needs;
+//    KV cache) as 1-KB chunks through a ring of kDepth LDS slots filled by
+//    global_load_lds DMAs; the load cursor is wave-uniform (scalar
+//    registers) and runs ahead of the consumer across phase boundaries, so
+//    weight bytes keep flowing while a wave waits for the activation it
+//    needs;
 //  * cross-workgroup dependencies use self-validating 64-bit words (32-bit
 //    payload + 32-bit step epoch) written and polled with agent-scope relaxed
 //    atomics: a consumer waits on the data itself, not on a counter followed
@@ -36,7 +38,10 @@ constexpr int kDepth = kRingDepth;  // 1-KB wave units in flight per wave (LDS r
 // s_waitcnt immediate that waits until at most kDepth-1 vector memory
 // operations are outstanding (expcnt and lgkmcnt left at their maximum)
 constexpr int kWaitRing = ((kDepth - 1) & 15) | (((kDepth - 1) >> 4) << 14) | (7 << 4) | (15 << 8);
+constexpr int kWaitRing2 = ((kDepth - 2) & 15) | (((kDepth - 2) >> 4) << 14) | (7 << 4) | (15 << 8);
+constexpr int kWaitRing4 = ((kDepth - 4) & 15) | (((kDepth - 4) >> 4) << 14) | (7 << 4) | (15 << 8);
 constexpr int kWaitAllVm = (7 << 4) | (15 << 8);
+static_assert(kDepth >= 4 && kDepth <= 32, "ring depth");
 // s_waitcnt immediate for lgkmcnt(0) only (vmcnt and expcnt at their maximum)
 constexpr int kWaitLgkm = 15 | (3 << 14) | (7 << 4);
 
@@ -100,13 +105,16 @@ KIE_DI float h2f_lo(uint32_t u) { return __half2float(__ushort_as_half((unsigned
 KIE_DI float h2f_hi(uint32_t u) { return __half2float(__ushort_as_half((unsigned short)(u >> 16))); }
 KIE_DI float hbits2f(uint16_t u) { return __half2float(__ushort_as_half(u)); }
 
-// swizzled position of element k of a GEMV input vector in LDS: inside each
-// 512-element block the first 4 of every lane's 8 elements are contiguous
-// across lanes, then the last 4, so each 16-byte LDS read is conflict-free
-KIE_DI int xs_pos(int k) {
-  const int b = k >> 9, e = k & 511;
-  return (b << 9) + (((e >> 2) & 1) << 8) + ((e >> 3) << 2) + (e & 3);
-}
+// position of element k of a GEMV input vector in LDS: element 8g + j sits
+// in plane j / 4 (planes `plane` floats apart) at float 4g + j % 4, so the
+// 16-byte reads of lanes with consecutive g are conflict-free
+KIE_DI int xs_pos(int k, int plane) { return ((k >> 2) & 1) * plane + ((k >> 3) << 2) + (k & 3); }
+
+// Wave-uniform values must be provably uniform to the compiler: a value it
+// thinks may differ between lanes turns every branch on it into a divergent
+// one, and a loop with a possibly divergent exit makes all its loop-carried
+// state (the load cursor, the ring slot) per-lane vector values.
+KIE_DI int rfl(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 // combine (m, l, acc) with (mo, lo, ao); m in log2 units, -inf = empty
 KIE_DI void lse_merge(float& m, float& l, float* acc, float mo, float lo, const float* ao) {
@@ -160,12 +168,18 @@ struct Dev {
   int wg, nwg, wave, lane, tid;
   Shared* sh;
   int* desc;
-  uint4* ring;  // this wave's kDepth x 1 KB LDS ring
+  uint4* ring;        // this wave's kDepth x 1 KB LDS ring
+  uint32_t ring_lane; // LDS byte address of this lane's 16 bytes in ring slot 0
+  int lane16;         // lane * 16
+  int plane;          // floats between the two planes of a GEMV input
   int32_t* state;
   u64 *X, *Q, *KC, *VC, *REC, *OB, *HB, *LMP;
   const float2* rope;
   int lpk, kpl, kl, dl, lane_active;
 };
+
+// the workgroup's abort flag, read after a barrier (uniform)
+KIE_DI bool aborted(const Dev& D) { return rfl(*(volatile int*)&D.sh->abort) != 0; }
 
 KIE_DI void raise_status(const Dev& D, int code) {
   atomicCAS(&D.state[0], 0, code);
@@ -240,8 +254,10 @@ KIE_DI bool poll_words(const Dev& D, const u64* base, int stride, uint32_t mask,
 }
 
 // the workgroup polls words [0, n) of src into dst (swizzled for GEMV input)
+// the workgroup polls words [0, n) of src into dst (planes for a GEMV input)
 template <bool SWZ>
 KIE_DI void poll_to_lds(const Dev& D, const u64* src, float* dst, int n, uint32_t epoch) {
+  const int plane = D.plane;
   for (int base = D.tid; base < n; base += kThreads * 8) {
     uint32_t mask = 0;
 #pragma unroll
@@ -252,7 +268,7 @@ KIE_DI void poll_to_lds(const Dev& D, const u64* src, float* dst, int n, uint32_
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const int i = base + k * kThreads;
-      if (i < n) dst[SWZ ? xs_pos(i) : i] = ll_f(v[k]);
+      if (i < n) dst[SWZ ? xs_pos(i, plane) : i] = ll_f(v[k]);
     }
   }
 }
@@ -273,18 +289,19 @@ KIE_DI uint64_t matrix_offset(const KParams& p, int kind) {
 // one wave's share of GEMV `kind` -> its 8-int descriptor (and the workgroup's rows)
 KIE_DI void write_gemv_desc(const KParams& p, int kind, int nwg, int wg, int wave, int* dsc, int* wgrows) {
   const GemvShape sh = gemv_shape(p.m, kind);
-  int r0, r1, u0, u1;
+  int r0, r1, c0, c1;
   gemv_rows(p.m, kind, nwg, wg, &r0, &r1);
-  gemv_wave_units(r1 - r0, sh.K, wave, &u0, &u1);
-  const int nb = blocks_per_row(sh.K);
-  const uint64_t off = matrix_offset(p, kind) + (uint64_t)(r0 + u0 / nb) * (uint64_t)sh.K;
+  gemv_wave_chunks(r1 - r0, sh.K, wave, &c0, &c1);
+  const int rs = row_stride(sh.K);
+  const int e0 = c0 * kBlock;
+  const uint64_t off = matrix_offset(p, kind) + (uint64_t)r0 * (uint64_t)rs + (uint64_t)e0;
   dsc[0] = (int)(uint32_t)off;
   dsc[1] = (int)(uint32_t)(off >> 32);
-  dsc[2] = u0 % nb;
-  dsc[3] = u1 - u0;
-  dsc[4] = nb;
-  dsc[5] = sh.K / 8;
-  dsc[6] = u0 / nb;
+  dsc[2] = c1 - c0;
+  dsc[3] = e0 / rs;
+  dsc[4] = e0 % rs;
+  dsc[5] = rs;
+  dsc[6] = 0;
   dsc[7] = 0;
   if (wave == 0) {
     wgrows[0] = r0;
@@ -326,57 +343,63 @@ KIE_DI void write_attn_desc(const KParams& p, int nwg, int wg, int wave, int kpl
 }
 
 // ---------------------------------------------------------------------------
-// the load cursor: walks this wave's unit sequence (weights and KV rows) over
-// the whole launch and issues exactly one 16-byte-per-lane load per call
+// the load cursor: walks this wave's chunk sequence (weights and KV rows) and
+// issues exactly one 1-KB chunk load into the ring per call.  All of its
+// state is wave-uniform, so it lives in scalar registers; a chunk load is a
+// scalar address step plus one global_load_lds with the lane's fixed offset.
 // ---------------------------------------------------------------------------
 struct Cursor {
-  int s, ph, nph, rem, kind, done;
-  const uint4* rowp;  // gemv: current row
-  int b, nb, K8;
-  int st, kvh, ka, kc, nst;  // attention: current segment
-  const uint16_t* kb;
-  const uint16_t* vb;
-  int seg1, l;  // attention: segment 1 still to come; layer
+  uint64_t base;    // byte address of the next chunk (attention: next K chunk)
+  uint64_t voff;    // attention: V chunk address minus K chunk address
+  uint32_t stride;  // bytes from one chunk (attention: key step) to the next
+  int rem;          // chunks left in this stretch (attention: 2 per key step)
+  int attn, kvh, seg, ph, nph, done;
 };
+
+// attention segment sg of layer l of this step (an empty one has rem 0)
+KIE_DI void cursor_attn_seg(const Dev& D, Cursor& c, int l, int sg) {
+  const KParams& p = *D.p;
+  const int* a = D.desc + D.wave * kWaveDesc + kConsumerAttn + 5 * sg;
+  const int g = rfl(a[0]), ka = rfl(a[1]), nst = rfl(a[3]);
+  c.seg = sg;
+  c.rem = 2 * nst;
+  c.kvh = 0;
+  c.base = (uint64_t)(uintptr_t)p.kv + 2 * (kv_offset(p.m, l, 0, g) + (uint64_t)ka * (uint64_t)p.m.hd);
+}
 
 KIE_DI void cursor_enter(const Dev& D, Cursor& c) {
   const KParams& p = *D.p;
   const int lmph = 5 * p.m.L;
   const int kind = c.ph == lmph ? PH_LM : phase_kind(p.m.parallel, c.ph % 5);
   const int l = c.ph == lmph ? 0 : c.ph / 5;
-  c.kind = kind;
-  c.l = l;
   if (kind == PH_ATTN) {
-    const int* a = D.desc + D.wave * kWaveDesc + kConsumerAttn;
-    const int nst0 = a[3], nst1 = a[8];
-    const bool first = nst0 > 0;
-    const int g = first ? a[0] : a[5];
-    c.st = 0;
-    c.kvh = 0;
-    c.rem = 2 * (nst0 + nst1);
-    c.ka = first ? a[1] : a[6];
-    c.kc = first ? a[2] : a[7];
-    c.nst = first ? nst0 : nst1;
-    c.seg1 = first && nst1 > 0;
-    c.kb = p.kv + kv_offset(p.m, l, 0, g);
-    c.vb = p.kv + kv_offset(p.m, l, 1, g);
+    c.attn = 1;
+    c.stride = (uint32_t)(attn_kpl(p.m.hd) * p.m.hd * 2);
+    c.voff = 2 * (kv_offset(p.m, 0, 1, 0) - kv_offset(p.m, 0, 0, 0));
+    cursor_attn_seg(D, c, l, 0);
     return;
   }
   const int* g = D.desc + D.wave * kWaveDesc + 8 * gemv_index(kind);
-  const uint64_t off = (uint64_t)(uint32_t)g[0] | ((uint64_t)(uint32_t)g[1] << 32);
-  c.rowp = (const uint4*)(p.W + (kind == PH_LM ? 0 : (uint64_t)l * p.pl.layer_stride) + off);
-  c.b = g[2];
-  c.rem = g[3];
-  c.nb = g[4];
-  c.K8 = g[5];
+  const uint64_t off = (uint64_t)(uint32_t)rfl(g[0]) | ((uint64_t)(uint32_t)rfl(g[1]) << 32);
+  c.attn = 0;
+  c.kvh = 0;
+  c.seg = 0;
+  c.voff = 0;
+  c.stride = kChunkBytes;
+  c.base = (uint64_t)(uintptr_t)p.W + 2 * ((kind == PH_LM ? 0 : (uint64_t)l * p.pl.layer_stride) + off);
+  c.rem = rfl(g[2]);
 }
 
 // The cursor never crosses into the next step by itself: the next step reads
 // KV-cache rows written during this step, which are only visible after the
 // end-of-step acquire.  At the end of its step it issues harmless loads until
-// the consumer restarts it (cursor_restart) after that acquire.
+// the consumer restarts it after that acquire.
 KIE_DI void cursor_advance(const Dev& D, Cursor& c) {
   while (c.rem == 0 && !c.done) {
+    if (c.attn && c.seg == 0) {
+      cursor_attn_seg(D, c, c.ph / 5, 1);
+      continue;
+    }
     if (++c.ph >= c.nph) {
       c.done = 1;
       break;
@@ -385,103 +408,281 @@ KIE_DI void cursor_advance(const Dev& D, Cursor& c) {
   }
 }
 
-// issue the next unit of the sequence into ring slot `slot` (one DMA per call)
+KIE_DI void dma_chunk(const Dev& D, uint64_t a, int slot);
+
+// issue the next chunk into ring slot `slot` (one DMA per call).  A chunk
+// may run past the end of its stretch (the last one of a workgroup's rows,
+// keys past the context, lanes past the keys of a step); those bytes stay in
+// the buffer (it ends in a zero tail) and the consumer discards them.
 KIE_DI void cursor_issue(const Dev& D, Cursor& c, int slot) {
-  const KParams& p = *D.p;
   if (c.rem == 0) cursor_advance(D, c);
-  // A lane with nothing to load reads the first packed kilobyte, which holds
-  // finite fp16 values: its GEMV input element is zero and its attention key
-  // is masked to probability 0, so it contributes exactly nothing.
-  const uint4* a = (const uint4*)p.W + D.lane;
+  uint64_t a = (uint64_t)(uintptr_t)D.p->W;  // after the step: the first packed kilobyte
   if (!c.done) {
-    if (c.kind == PH_ATTN) {
-      const int key = c.ka + c.st * D.kpl + D.kl;
-      if (D.lane_active && key < c.kc) a = (const uint4*)((c.kvh ? c.vb : c.kb) + (uint64_t)key * p.m.hd) + D.dl;
-      if (c.kvh) {
-        if (++c.st == c.nst && c.seg1) {
-          const int* s1 = D.desc + D.wave * kWaveDesc + kConsumerAttn + 5;
-          c.seg1 = 0;
-          c.st = 0;
-          c.ka = s1[1];
-          c.kc = s1[2];
-          c.nst = s1[3];
-          c.kb = p.kv + kv_offset(p.m, c.l, 0, s1[0]);
-          c.vb = p.kv + kv_offset(p.m, c.l, 1, s1[0]);
-        }
-      }
-      c.kvh ^= 1;
-    } else {
-      const int sg = c.b * kBlock8 + D.lane;
-      if (sg < c.K8) a = c.rowp + sg;  // the input tail of xs is zero for the others
-      if (++c.b == c.nb) {
-        c.b = 0;
-        c.rowp += c.K8;
-      }
-    }
+    a = c.base + (c.kvh ? c.voff : 0);
+    if (c.kvh || !c.attn) c.base += c.stride;
+    c.kvh ^= c.attn;
     --c.rem;
   }
-  // 16 bytes per lane straight into LDS: lane i lands at slot + 16 i
-  __builtin_amdgcn_global_load_lds((const void*)a, (__attribute__((address_space(3))) void*)(D.ring + slot * kWave),
-                                   16, 0, 2 /* nt */);
+  dma_chunk(D, a, slot);
 }
 
-// read this lane's 16 bytes of ring slots.  The reads are written as asm and
-// wait for themselves, so the compiler neither sees an LDS access that the
-// ring DMAs could alias nor leaves an output register in flight.
-KIE_DI uint32_t ring_addr(const Dev& D, int slot) {
-  return (uint32_t)(uintptr_t)(D.ring + slot * kWave + D.lane);
+// Re-assert that the cursor and the ring slot are wave-uniform (they are;
+// readfirstlane makes it visible to the compiler, so the stream loops keep
+// them in scalar registers and branch on them with scalar branches).
+KIE_DI uint64_t rfl64(uint64_t v) {
+  return (uint64_t)(uint32_t)rfl((int)(uint32_t)v) | ((uint64_t)(uint32_t)rfl((int)(uint32_t)(v >> 32)) << 32);
 }
-KIE_DI uint4 ring_read(const Dev& D, int slot) {
-  uint4 x;
-  asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(x) : "v"(ring_addr(D, slot)) : "memory");
-  return x;
+KIE_DI void make_uniform(Cursor& c, int& slot) {
+  c.base = rfl64(c.base);
+  c.voff = rfl64(c.voff);
+  c.stride = (uint32_t)rfl((int)c.stride);
+  c.rem = rfl(c.rem);
+  c.attn = rfl(c.attn);
+  c.kvh = rfl(c.kvh);
+  c.seg = rfl(c.seg);
+  c.ph = rfl(c.ph);
+  c.nph = rfl(c.nph);
+  c.done = rfl(c.done);
+  slot = rfl(slot);
 }
-KIE_DI void ring_read4(const Dev& D, int s0, int s1, int s2, int s3, uint4& x0, uint4& x1, uint4& x2, uint4& x3) {
+
+KIE_DI int ring_next(int s) { return s + 1 == kDepth ? 0 : s + 1; }
+KIE_DI int ring_add(int s, int k) { return s + k >= kDepth ? s + k - kDepth : s + k; }
+KIE_DI uint32_t ring_addr(const Dev& D, int slot) { return D.ring_lane + (uint32_t)slot * kChunkBytes; }
+
+KIE_DI void dma_chunk(const Dev& D, uint64_t a, int slot) {
+  // 16 bytes per lane straight into LDS: lane i lands at slot + 16 i
+  __builtin_amdgcn_global_load_lds((const void*)((const char*)(uintptr_t)a + D.lane16),
+                                   (__attribute__((address_space(3))) void*)(D.ring + slot * kWave), 16, 0,
+                                   2 /* nt */);
+}
+
+// issue the next four chunks into slots slot .. slot+3.  Inside one stretch
+// (four GEMV chunks, or two whole attention key steps) that is four scalar
+// address steps; otherwise it falls back to one cursor_issue per chunk.
+KIE_DI void cursor_issue4(const Dev& D, Cursor& c, int slot) {
+  if (!c.done && c.rem >= 4 && c.kvh == 0) {
+    const uint64_t b = c.base;
+    const uint64_t s1 = c.attn ? c.voff : (uint64_t)kChunkBytes;
+    const uint64_t s2 = c.attn ? (uint64_t)c.stride : 2ull * kChunkBytes;
+    dma_chunk(D, b, slot);
+    dma_chunk(D, b + s1, ring_add(slot, 1));
+    dma_chunk(D, b + s2, ring_add(slot, 2));
+    dma_chunk(D, b + s2 + s1, ring_add(slot, 3));
+    c.base = b + 2 * s2;
+    c.rem -= 4;
+  } else {
+#pragma unroll 1
+    for (int k = 0; k < 4; ++k) cursor_issue(D, c, ring_add(slot, k));
+  }
+}
+
+typedef float f4v __attribute__((ext_vector_type(4)));
+typedef unsigned u4v __attribute__((ext_vector_type(4)));
+
+// LDS reads of ring slots are written as asm that waits for itself: the
+// compiler then neither sees an LDS access that an in-flight ring DMA could
+// alias (it would drain every DMA first) nor leaves an output register in
+// flight.  A GEMV chunk reads its weights and the lane's two input halves in
+// one round trip.
+KIE_DI void read_w_x(uint32_t ra, uint32_t xa, uint32_t xb, u4v& w, f4v& a, f4v& b) {
+  asm volatile(
+      "ds_read_b128 %0, %3\n\t"
+      "ds_read_b128 %1, %4\n\t"
+      "ds_read_b128 %2, %5\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(w), "=&v"(a), "=&v"(b)
+      : "v"(ra), "v"(xa), "v"(xb)
+      : "memory");
+}
+// four GEMV chunks: weights of four ring slots and the input halves of each
+KIE_DI void read_w_x4(const uint32_t (&r)[4], const uint32_t (&x)[8], u4v (&w)[4], f4v (&a)[4], f4v (&b)[4]) {
+  asm volatile(
+      "ds_read_b128 %0, %12\n\t"
+      "ds_read_b128 %4, %16\n\t"
+      "ds_read_b128 %8, %17\n\t"
+      "ds_read_b128 %1, %13\n\t"
+      "ds_read_b128 %5, %18\n\t"
+      "ds_read_b128 %9, %19\n\t"
+      "ds_read_b128 %2, %14\n\t"
+      "ds_read_b128 %6, %20\n\t"
+      "ds_read_b128 %10, %21\n\t"
+      "ds_read_b128 %3, %15\n\t"
+      "ds_read_b128 %7, %22\n\t"
+      "ds_read_b128 %11, %23\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(w[0]), "=&v"(w[1]), "=&v"(w[2]), "=&v"(w[3]), "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3]),
+        "=&v"(b[0]), "=&v"(b[1]), "=&v"(b[2]), "=&v"(b[3])
+      : "v"(r[0]), "v"(r[1]), "v"(r[2]), "v"(r[3]), "v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]), "v"(x[4]), "v"(x[5]),
+        "v"(x[6]), "v"(x[7])
+      : "memory");
+}
+// two attention key steps: K, V, K, V of four consecutive slots
+KIE_DI void read_kv2(const uint32_t (&r)[4], u4v (&x)[4]) {
   asm volatile(
       "ds_read_b128 %0, %4\n\t"
       "ds_read_b128 %1, %5\n\t"
       "ds_read_b128 %2, %6\n\t"
       "ds_read_b128 %3, %7\n\t"
       "s_waitcnt lgkmcnt(0)"
-      : "=&v"(x0), "=&v"(x1), "=&v"(x2), "=&v"(x3)
-      : "v"(ring_addr(D, s0)), "v"(ring_addr(D, s1)), "v"(ring_addr(D, s2)), "v"(ring_addr(D, s3))
+      : "=&v"(x[0]), "=&v"(x[1]), "=&v"(x[2]), "=&v"(x[3])
+      : "v"(r[0]), "v"(r[1]), "v"(r[2]), "v"(r[3])
+      : "memory");
+}
+KIE_DI void read_kv(uint32_t rk, uint32_t rv, u4v& k, u4v& v) {
+  asm volatile(
+      "ds_read_b128 %0, %2\n\t"
+      "ds_read_b128 %1, %3\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(k), "=&v"(v)
+      : "v"(rk), "v"(rv)
       : "memory");
 }
 
-KIE_DI int ring_next(int s) { return s + 1 == kDepth ? 0 : s + 1; }
+KIE_DI void unpack8(const u4v x, float* v) {
+  v[0] = h2f_lo(x.x); v[1] = h2f_hi(x.x); v[2] = h2f_lo(x.y); v[3] = h2f_hi(x.y);
+  v[4] = h2f_lo(x.z); v[5] = h2f_hi(x.z); v[6] = h2f_lo(x.w); v[7] = h2f_hi(x.w);
+}
 
 // ---------------------------------------------------------------------------
-// the ring: consume the next n units.  Exactly one DMA is issued per unit
-// consumed, so when units c..c+3 are read the kDepth-4 younger DMAs may stay
-// in flight (vector memory reads complete in order).  Units are taken four at
-// a time so that one LDS round trip serves four of them.
+// GEMV stream: consume this wave's nch chunks of the workgroup's packed rows
+// (row stride rs; the first chunk starts at column S of row R) and write one
+// partial sum per (row, wave) into part.  A chunk meets at most two rows: the
+// lanes still in row R finish it, the others start row R + 1.
 // ---------------------------------------------------------------------------
-constexpr int kWaitRing4 = ((kDepth - 4) & 15) | (((kDepth - 4) >> 4) << 14) | (7 << 4) | (15 << 8);
+// one chunk's dot product, chained onto `init`
+KIE_DI float dot_chunk(const u4v w, const f4v a, const f4v b, float init) {
+  float t = init;
+  t = __builtin_fmaf(h2f_lo(w.x), a.x, t);
+  t = __builtin_fmaf(h2f_hi(w.x), a.y, t);
+  t = __builtin_fmaf(h2f_lo(w.y), a.z, t);
+  t = __builtin_fmaf(h2f_hi(w.y), a.w, t);
+  t = __builtin_fmaf(h2f_lo(w.z), b.x, t);
+  t = __builtin_fmaf(h2f_hi(w.z), b.y, t);
+  t = __builtin_fmaf(h2f_lo(w.w), b.z, t);
+  t = __builtin_fmaf(h2f_hi(w.w), b.w, t);
+  return t;
+}
 
-template <class F>
-KIE_DI void run_units(const Dev& D, Cursor& cur, int& slot, int n, F& consume) {
-  int j = 0;
-  for (; j + 4 <= n; j += 4) {
-    __builtin_amdgcn_s_waitcnt(kWaitRing4);
-    const int s0 = slot, s1 = ring_next(s0), s2 = ring_next(s1), s3 = ring_next(s2);
-    uint4 x0, x1, x2, x3;
-    ring_read4(D, s0, s1, s2, s3, x0, x1, x2, x3);
-    cursor_issue(D, cur, s0);
-    cursor_issue(D, cur, s1);
-    cursor_issue(D, cur, s2);
-    cursor_issue(D, cur, s3);
-    slot = ring_next(s3);
-    consume(x0, j, false);
-    consume(x1, j + 1, false);
-    consume(x2, j + 2, false);
-    consume(x3, j + 3, j + 3 == n - 1);
+struct GemvAcc {
+  float* part;
+  float A;
+  int R, S, rs, wave, lane8, lane;
+  // fold one chunk (row R from column S) into the accumulator
+  KIE_DI void chunk(const u4v w, const f4v a, const f4v b) {
+    const bool inR = S + lane8 < rs;
+    const float t = dot_chunk(w, a, b, inR ? A : 0.f);
+    if (S + kBlock < rs) {
+      A = t;
+      S += kBlock;
+    } else {
+      // row R ends in this chunk (lanes past its end already hold row R + 1)
+      const float sum = wave_sum(inR ? t : 0.f);
+      if (lane == 0) part[R * kWaves + wave] = sum;
+      A = inR ? 0.f : t;
+      ++R;
+      S += kBlock - rs;
+    }
   }
-  for (; j < n; ++j) {
+};
+
+KIE_DI void gemv_stream(const Dev& D, Cursor& cur, int& slot, const float* xs, float* part, int nch, int R, int S,
+                        int rs, int nrows) {
+  make_uniform(cur, slot);
+  const uint32_t xs0 = (uint32_t)(uintptr_t)xs;
+  const uint32_t pb = (uint32_t)D.plane * 4u;
+  GemvAcc g{part, 0.f, R, S, rs, D.wave, D.lane * 8, D.lane};
+  int j = 0;
+  if (rs >= 4 * kBlock) {
+    // four chunks per LDS round trip; they meet at most two rows
+    for (; j + 4 <= nch; j += 4) {
+      uint32_t ra[4], xa[8];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int er = g.S + k * kBlock + g.lane8;
+        const int col = er < rs ? er : er - rs;
+        xa[2 * k] = xs0 + (uint32_t)col * 2u;
+        xa[2 * k + 1] = xa[2 * k] + pb;
+        ra[k] = ring_addr(D, ring_add(slot, k));
+      }
+      __builtin_amdgcn_s_waitcnt(kWaitRing4);
+      u4v w[4];
+      f4v a[4], b[4];
+      read_w_x4(ra, xa, w, a, b);
+      cursor_issue4(D, cur, slot);
+      slot = ring_add(slot, 4);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) g.chunk(w[k], a[k], b[k]);
+    }
+  }
+  for (; j < nch; ++j) {
+    const int er = g.S + g.lane8;
+    const int col = er < rs ? er : er - rs;
+    const uint32_t xa = xs0 + (uint32_t)col * 2u;  // float4 number col/8 of plane 0
     __builtin_amdgcn_s_waitcnt(kWaitRing);
-    const uint4 x = ring_read(D, slot);
+    u4v w;
+    f4v a, b;
+    read_w_x(ring_addr(D, slot), xa, xa + pb, w, a, b);
     cursor_issue(D, cur, slot);
     slot = ring_next(slot);
-    consume(x, j, j == n - 1);
+    g.chunk(w, a, b);
+  }
+  if (g.S > 0 && g.R < nrows) {
+    const float sum = wave_sum(g.A);
+    if (D.lane == 0) part[g.R * kWaves + D.wave] = sum;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// attention stream: nst key steps of one segment; a step is a K chunk and a
+// V chunk of the same kpl keys (lpk lanes per key, 8 dims per lane), folded
+// into every key slot's online softmax
+// ---------------------------------------------------------------------------
+template <int G>
+KIE_DI void attn_step(const Dev& D, const u4v kx, const u4v vx, int key, int kc, const float (&q)[G][8],
+                      float (&mrow)[G], float (&lrow)[G], float (&acc)[G][8]) {
+  const bool ok = D.lane_active && key < kc;
+  float k8[8], v8[8];
+  unpack8(kx, k8);
+  unpack8(vx, v8);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v8[e] = ok ? v8[e] : 0.f;  // bytes past the keys may be anything
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float t = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) t = __builtin_fmaf(k8[e], q[h][e], t);
+    t = group_sum(t, D.lpk);
+    online_update(mrow[h], lrow[h], acc[h], ok ? t : -INFINITY, v8);
+  }
+}
+
+template <int G>
+KIE_DI void attn_stream(const Dev& D, Cursor& cur, int& slot, int nst, int ka, int kc, const float (&q)[G][8],
+                        float (&mrow)[G], float (&lrow)[G], float (&acc)[G][8]) {
+  make_uniform(cur, slot);
+  int st = 0;
+  for (; st + 2 <= nst; st += 2) {
+    uint32_t ra[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) ra[k] = ring_addr(D, ring_add(slot, k));
+    __builtin_amdgcn_s_waitcnt(kWaitRing4);
+    u4v x[4];
+    read_kv2(ra, x);
+    cursor_issue4(D, cur, slot);
+    slot = ring_add(slot, 4);
+    attn_step<G>(D, x[0], x[1], ka + st * D.kpl + D.kl, kc, q, mrow, lrow, acc);
+    attn_step<G>(D, x[2], x[3], ka + (st + 1) * D.kpl + D.kl, kc, q, mrow, lrow, acc);
+  }
+  if (st < nst) {
+    __builtin_amdgcn_s_waitcnt(kWaitRing2);
+    const int sv = ring_next(slot);
+    u4v kx, vx;
+    read_kv(ring_addr(D, slot), ring_addr(D, sv), kx, vx);
+#pragma unroll 1
+    for (int k = 0; k < 2; ++k) cursor_issue(D, cur, ring_add(slot, k));
+    slot = ring_next(sv);
+    attn_step<G>(D, kx, vx, ka + st * D.kpl + D.kl, kc, q, mrow, lrow, acc);
   }
 }
 
@@ -489,7 +690,19 @@ KIE_DI void run_units(const Dev& D, Cursor& cur, int& slot, int n, F& consume) {
 // prologue helpers
 // ---------------------------------------------------------------------------
 // xraw -> xs = g * x / sqrt(mean(x^2) + eps), swizzled, zero tail to nb*512
-KIE_DI void rmsnorm_to_xs(const Dev& D, const float* xraw, const uint16_t* g, float* xs) {
+// this thread's RMSNorm gains (elements tid + k * kThreads), loaded into
+// registers before the input is polled so that their latency overlaps it
+KIE_DI void load_gains(const Dev& D, const uint16_t* g, float (&gr)[kGainRegs]) {
+  const int d = D.p->m.d;
+#pragma unroll
+  for (int k = 0; k < kGainRegs; ++k) {
+    const int i = D.tid + k * kThreads;
+    gr[k] = i < d ? hbits2f(g[i]) : 0.f;
+  }
+  asm volatile("" ::: "memory");  // issue the loads here, ahead of the poll
+}
+
+KIE_DI void rmsnorm_to_xs(const Dev& D, const float* xraw, const float (&gr)[kGainRegs], float* xs) {
   const KParams& p = *D.p;
   const int d = p.m.d;
   float ss = 0.f;
@@ -501,82 +714,19 @@ KIE_DI void rmsnorm_to_xs(const Dev& D, const float* xraw, const uint16_t* g, fl
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) tot += D.sh->redf[w];
   const float inv = 1.0f / sqrtf(tot / (float)d + p.m.eps);
-  const int padded = blocks_per_row(d) * kBlock;
-  for (int i = D.tid; i < padded; i += kThreads) {
-    float v = 0.f;
-    if (i < d) v = xraw[i] * inv * hbits2f(g[i]);
-    xs[xs_pos(i)] = v;
+  const int padded = row_stride(d);
+#pragma unroll
+  for (int k = 0; k < kGainRegs; ++k) {
+    const int i = D.tid + k * kThreads;
+    if (i < padded) xs[xs_pos(i, D.plane)] = i < d ? xraw[i] * inv * gr[k] : 0.f;
   }
 }
 
+// the zero columns of a padded row (row_stride(K) > K)
 KIE_DI void zero_tail(const Dev& D, float* xs, int K) {
-  const int padded = blocks_per_row(K) * kBlock;
-  for (int i = K + D.tid; i < padded; i += kThreads) xs[xs_pos(i)] = 0.f;
+  const int padded = row_stride(K);
+  for (int i = K + D.tid; i < padded; i += kThreads) xs[xs_pos(i, D.plane)] = 0.f;
 }
-
-// one GEMV phase's consumer: dot a 512-column block with the LDS input and
-// write one partial row sum per (row, wave)
-struct GemvConsume {
-  const float4* xs4;
-  float* part;
-  int r, b, nb, lane, wave;
-  float acc;
-  KIE_DI void operator()(const uint4 x, int, bool last) {
-    const float4 xa = xs4[b * 128 + lane];
-    const float4 xb = xs4[b * 128 + 64 + lane];
-    float t = acc;
-    t = __builtin_fmaf(h2f_lo(x.x), xa.x, t);
-    t = __builtin_fmaf(h2f_hi(x.x), xa.y, t);
-    t = __builtin_fmaf(h2f_lo(x.y), xa.z, t);
-    t = __builtin_fmaf(h2f_hi(x.y), xa.w, t);
-    t = __builtin_fmaf(h2f_lo(x.z), xb.x, t);
-    t = __builtin_fmaf(h2f_hi(x.z), xb.y, t);
-    t = __builtin_fmaf(h2f_lo(x.w), xb.z, t);
-    t = __builtin_fmaf(h2f_hi(x.w), xb.w, t);
-    acc = t;
-    if (b == nb - 1 || last) {
-      const float sum = wave_sum(acc);
-      if (lane == 0) part[r * kWaves + wave] = sum;
-      acc = 0.f;
-    }
-    if (++b == nb) {
-      b = 0;
-      ++r;
-    }
-  }
-};
-
-// one attention segment's consumer: even units are 4..8 keys of K, odd units
-// the same keys of V; every key slot (lane group) keeps an online softmax
-template <int G>
-struct AttnConsume {
-  float (&mrow)[G];
-  float (&lrow)[G];
-  float (&acc)[G][8];
-  const float (&q)[G][8];
-  float (&sc)[G];
-  int ka, kc, kpl, kl, lpk, lane_active;
-  KIE_DI void operator()(const uint4 x, int u, bool) {
-    float v[8];
-    v[0] = h2f_lo(x.x); v[1] = h2f_hi(x.x); v[2] = h2f_lo(x.y); v[3] = h2f_hi(x.y);
-    v[4] = h2f_lo(x.z); v[5] = h2f_hi(x.z); v[6] = h2f_lo(x.w); v[7] = h2f_hi(x.w);
-    if ((u & 1) == 0) {
-      const int key = ka + (u >> 1) * kpl + kl;
-      const bool ok = lane_active && key < kc;
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        float t = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) t = __builtin_fmaf(v[e], q[h][e], t);
-        t = group_sum(t, lpk);
-        sc[h] = ok ? t : -INFINITY;
-      }
-    } else {
-#pragma unroll
-      for (int h = 0; h < G; ++h) online_update(mrow[h], lrow[h], acc[h], sc[h], v);
-    }
-  }
-};
 
 // ---------------------------------------------------------------------------
 // the kernel
@@ -584,7 +734,7 @@ struct AttnConsume {
 template <int G>
 __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
   // Two separate LDS objects: the ring, written only by DMAs and read only by
-  // ring_read(), and everything else.  Keeping them apart lets the compiler
+  // the ring-read asm, and everything else.  Keeping them apart lets the compiler
   // prove that ordinary LDS accesses never alias an in-flight ring DMA.
   __shared__ float lds_main[kMainFloats];
   __shared__ Shared sh_static;
@@ -600,6 +750,9 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
   D.lane = threadIdx.x & 63;
   D.sh = &sh_static;
   D.ring = ring_lds + D.wave * kDepth * kWave;
+  D.ring_lane = (uint32_t)(uintptr_t)(D.ring + D.lane);
+  D.lane16 = D.lane * 16;
+  D.plane = p.lp.kmax / 2;
   D.desc = (int*)(lds_dyn + p.lp.desc);
   D.state = (int32_t*)(p.ws + p.wl.state);
   D.X = (u64*)(p.ws + p.wl.X);
@@ -649,17 +802,16 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
 
   // cursor and ring (started at the top of every step)
   Cursor cur;
-  cur.s = 0;
+  cur.base = (uint64_t)(uintptr_t)p.W;
+  cur.voff = 0;
+  cur.stride = kChunkBytes;
+  cur.rem = 0;
+  cur.attn = 0;
+  cur.kvh = 0;
+  cur.seg = 0;
   cur.ph = 0;
   cur.nph = 0;
   cur.done = 1;
-  cur.rem = 0;
-  cur.kind = PH_QKV;
-  cur.st = 0; cur.kvh = 0; cur.ka = 0; cur.kc = 0; cur.nst = 0; cur.seg1 = 0; cur.l = 0;
-  cur.b = 0; cur.nb = 1; cur.K8 = 0;
-  cur.rowp = (const uint4*)p.W;
-  cur.kb = p.kv;
-  cur.vb = p.kv;
   int slot = 0;
 
   int token = 0;
@@ -679,12 +831,12 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
     // load has completed (the end-of-step polls waited for them), so the
     // slots can be reused in order from `slot`.
     __builtin_amdgcn_s_waitcnt(kWaitAllVm);
-    cur.s = s;
     cur.ph = 0;
     cur.nph = nphases(p, s);
     cur.done = 0;
     cursor_enter(D, cur);
-    for (int i = 0; i < kDepth; ++i) cursor_issue(D, cur, slot + i < kDepth ? slot + i : slot + i - kDepth);
+#pragma unroll 1
+    for (int i = 0; i < kDepth; ++i) cursor_issue(D, cur, ring_add(slot, i));
 
     // ---- input token and embedding ------------------------------------
     if (p.forced) {
@@ -714,7 +866,7 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
         spin_word(D, D.LMP + 2 * D.nwg - 1, 0xFFFFFFFFu, &dummy);
       }
       wg_sync();
-      if (D.sh->abort) { __builtin_amdgcn_s_waitcnt(kWaitAllVm); return; }
+      if (aborted(D)) { __builtin_amdgcn_s_waitcnt(kWaitAllVm); return; }
     }
 
     const int nph = nphases(p, s);
@@ -727,17 +879,16 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
       stamp(D, s, ph, 0);
       if (kind == PH_ATTN) {
         // ================= attention over the KV cache ==================
-        float mrow[G], lrow[G], acc[G][8], q[G][8], sc[G];
-        const int nseg = adesc[10];
+        float mrow[G], lrow[G], acc[G][8], q[G][8];
+        const int nseg = rfl(adesc[10]);
         for (int sg = 0; sg < nseg; ++sg) {
-          const int g = adesc[5 * sg + 0];
-          const int ka = adesc[5 * sg + 1], kc = adesc[5 * sg + 2], nst = adesc[5 * sg + 3];
-          const int has_pos = adesc[5 * sg + 4];
+          const int g = rfl(adesc[5 * sg + 0]);
+          const int ka = rfl(adesc[5 * sg + 1]), kc = rfl(adesc[5 * sg + 2]), nst = rfl(adesc[5 * sg + 3]);
+          const int has_pos = rfl(adesc[5 * sg + 4]);
 #pragma unroll
           for (int h = 0; h < G; ++h) {
             mrow[h] = -INFINITY;
             lrow[h] = 0.f;
-            sc[h] = -INFINITY;
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
           }
@@ -752,8 +903,7 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
               for (int e = 0; e < 8; ++e) q[h][e] = ll_f(qw[e]);
             }
           }
-          AttnConsume<G> ac{mrow, lrow, acc, q, sc, ka, kc, D.kpl, D.kl, D.lpk, D.lane_active};
-          run_units(D, cur, slot, 2 * nst, ac);
+          attn_stream<G>(D, cur, slot, nst, ka, kc, q, mrow, lrow, acc);
           if (has_pos) {
             // current key and value (fp16-rounded) from the QKV epilogue
             const u64* kp = D.KC + (uint64_t)l * kvd + (uint64_t)g * hd + D.dl * 8;
@@ -808,7 +958,7 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
         }
         stamp(D, s, ph, 1);
         wg_sync();
-        if (D.sh->abort) { __builtin_amdgcn_s_waitcnt(kWaitAllVm); return; }
+        if (aborted(D)) { __builtin_amdgcn_s_waitcnt(kWaitAllVm); return; }
         // workgroup merge of the waves -> one record per segment
         for (int sg = 0; sg < nseg; ++sg) {
           u64* rec = D.REC + (((uint64_t)l * D.nwg + D.wg) * 2 + sg) * G * (hd + 2);
@@ -833,7 +983,7 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
         stamp(D, s, ph, 2);
         // merger: the workgroup holding head g's last key combines the
         // records of every workgroup that met head g
-        const int merge_g = adesc[11];
+        const int merge_g = rfl(adesc[11]);
         if (merge_g >= 0) {
           const int g = merge_g;
           const int n_ctx = pos + 1;
@@ -911,7 +1061,7 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
             }
           }
           wg_sync();
-          if (D.sh->abort) { __builtin_amdgcn_s_waitcnt(kWaitAllVm); return; }
+          if (aborted(D)) { __builtin_amdgcn_s_waitcnt(kWaitAllVm); return; }
           // 3. combine: o = sum_r exp2(m_r - M) O_r / sum_r exp2(m_r - M) l_r
           for (int t = D.tid; t < G * hd; t += kThreads) {
             const int h = t / hd, dd = t % hd;
@@ -929,30 +1079,43 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
           }
         }
         wg_sync();
-        if (D.sh->abort) { __builtin_amdgcn_s_waitcnt(kWaitAllVm); return; }
+        if (aborted(D)) { __builtin_amdgcn_s_waitcnt(kWaitAllVm); return; }
         stamp(D, s, ph, 3);
         continue;
       }
 
       // ===================== GEMV phases =====================
       const int gi = gemv_index(kind);
-      const int r0 = wgrows[2 * gi], nrows = wgrows[2 * gi + 1];
+      const int r0 = rfl(wgrows[2 * gi]), nrows = rfl(wgrows[2 * gi + 1]);
       // prologue: the input vector
+      float gr[kGainRegs];
+      float2 rope_cs = make_float2(1.f, 0.f);
       if (kind == PH_QKV) {
+        load_gains(D, Wl + p.pl.attn_norm, gr);
+        // this thread's RoPE factors for the epilogue, fetched ahead too
+        if (2 * D.tid < nrows) {
+          const int rr = r0 + 2 * D.tid;
+          if (rr < qd + kvd) {
+            const int i = ((rr < qd ? rr : rr - qd) % hd) >> 1;
+            rope_cs = D.rope[(uint64_t)pos * (hd / 2) + i];
+          }
+        }
+        asm volatile("" ::: "memory");
         if (p.m.parallel ? (l > p.m.delay) : (l > 0)) {
           const int xi = p.m.parallel ? l : 2 * l;
           poll_to_lds<false>(D, D.X + (uint64_t)xi * d, xraw, d, epoch);
           wg_sync();
-          if (D.sh->abort) { __builtin_amdgcn_s_waitcnt(kWaitAllVm); return; }
+          if (aborted(D)) { __builtin_amdgcn_s_waitcnt(kWaitAllVm); return; }
         }
-        rmsnorm_to_xs(D, xraw, Wl + p.pl.attn_norm, xs);
+        rmsnorm_to_xs(D, xraw, gr, xs);
       } else if (kind == PH_GU) {
+        load_gains(D, Wl + p.pl.mlp_norm, gr);
         if (!p.m.parallel) {
           poll_to_lds<false>(D, D.X + (uint64_t)(2 * l + 1) * d, xraw, d, epoch);
           wg_sync();
-          if (D.sh->abort) { __builtin_amdgcn_s_waitcnt(kWaitAllVm); return; }
+          if (aborted(D)) { __builtin_amdgcn_s_waitcnt(kWaitAllVm); return; }
         }
-        rmsnorm_to_xs(D, xraw, Wl + p.pl.mlp_norm, xs);
+        rmsnorm_to_xs(D, xraw, gr, xs);
       } else if (kind == PH_O) {
         poll_to_lds<true>(D, D.OB + (uint64_t)l * qd, xs, qd, epoch);
         zero_tail(D, xs, qd);
@@ -960,20 +1123,20 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
         poll_to_lds<true>(D, D.HB + (uint64_t)l * F, xs, F, epoch);
         zero_tail(D, xs, F);
       } else {  // LM
+        load_gains(D, p.W + p.pl.final_norm, gr);
         poll_to_lds<false>(D, D.X + (uint64_t)(2 * L) * d, xraw, d, epoch);
         wg_sync();
-        if (D.sh->abort) { __builtin_amdgcn_s_waitcnt(kWaitAllVm); return; }
-        rmsnorm_to_xs(D, xraw, p.W + p.pl.final_norm, xs);
+        if (aborted(D)) { __builtin_amdgcn_s_waitcnt(kWaitAllVm); return; }
+        rmsnorm_to_xs(D, xraw, gr, xs);
       }
       for (int i = D.tid; i < nrows * kWaves; i += kThreads) part[i] = 0.f;
       wg_sync();
-      if (D.sh->abort) { __builtin_amdgcn_s_waitcnt(kWaitAllVm); return; }
+      if (aborted(D)) { __builtin_amdgcn_s_waitcnt(kWaitAllVm); return; }
       stamp(D, s, ph, 1);
 
       {
         const int* gd = D.desc + D.wave * kWaveDesc + 8 * gi;
-        GemvConsume c{(const float4*)xs, part, gd[6], gd[2], gd[4], D.lane, D.wave, 0.f};
-        run_units(D, cur, slot, gd[3], c);
+        gemv_stream(D, cur, slot, xs, part, rfl(gd[2]), rfl(gd[3]), rfl(gd[4]), rfl(gd[5]), nrows);
       }
       stamp(D, s, ph, 2);
       wg_sync();
@@ -995,7 +1158,7 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
             const int base = isq ? 0 : qd;
             const int head = (rr - base) / hd;
             const int i = ((rr - base) % hd) >> 1;
-            const float2 cs = rp[i];
+            const float2 cs = t == D.tid ? rope_cs : rp[i];
             const float a = y0 * cs.x - y1 * cs.y;
             const float b = y0 * cs.y + y1 * cs.x;
             if (isq) {
@@ -1141,7 +1304,7 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
       __builtin_amdgcn_s_waitcnt(kWaitAllVm);
     }
     wg_sync();
-    if (D.sh->abort) { __builtin_amdgcn_s_waitcnt(kWaitAllVm); return; }
+    if (aborted(D)) { __builtin_amdgcn_s_waitcnt(kWaitAllVm); return; }
     stamp(D, s, tph, 1);
     if (lm) {
       if (D.tid == 0) {

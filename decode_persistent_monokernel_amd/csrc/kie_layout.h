@@ -19,8 +19,10 @@ namespace kie {
 constexpr int kWave = 64;               // lanes per wavefront (CDNA)
 constexpr int kWaves = 8;               // wavefronts per workgroup
 constexpr int kThreads = kWave * kWaves;
-constexpr int kBlock = 512;             // fp16 elements one wave reads with 16 B per lane
-constexpr int kBlock8 = kBlock / 8;     // 16-byte segments per block (= lanes)
+constexpr int kBlock = 512;             // fp16 elements one wave reads with 16 B per lane (a chunk)
+constexpr int kBlock8 = kBlock / 8;     // 16-byte segments per chunk (= lanes)
+constexpr int kChunkBytes = kBlock * 2;
+constexpr int kGainRegs = 8;            // RMSNorm gains per thread: d <= kGainRegs * kThreads
 
 enum PhaseKind : int { PH_QKV = 0, PH_ATTN = 1, PH_O = 2, PH_GU = 3, PH_DOWN = 4, PH_LM = 5 };
 
@@ -44,13 +46,20 @@ struct Dims {
 // Per layer, in order: attn_norm[d], Wqkv[(H+2Hkv)hd][d], Wo[d][H hd],
 // mlp_norm[d], Wgu[2F][d], Wd[d][F]; then final_norm[d], Wlm[V][d], E[V][d].
 // Matrices stay row-major [out][in] (a row is the contiguous K-vector one
-// output consumes) with two row permutations:
+// output consumes), rows kept apart by row_stride(K) elements (K itself, or
+// 512 with a zero tail when K < 512, so that a 1-KB chunk never spans more
+// than two rows), with two row permutations:
 //   * Wqkv: inside every q and k head, packed row 2i is dim i and row 2i+1 is
 //     dim i + hd/2, so the rotate-half RoPE pair of an output sits in one
 //     workgroup; v rows are in natural order;
 //   * Wgu: packed row 2f is gate row f, row 2f+1 is up row f.
-// Each tensor starts on a 256-byte boundary.
+// Each tensor starts on a 256-byte boundary; after the last one come kBlock
+// zero elements, so a chunk load that runs past a tensor's end stays inside
+// the buffer.  The embedding table keeps stride d (it is gathered, not
+// streamed).
 // ---------------------------------------------------------------------------
+KIE_HD int row_stride(int K) { return K < kBlock ? kBlock : K; }
+
 struct PackLayout {
   uint64_t layer_stride;
   uint64_t attn_norm, wqkv, wo, mlp_norm, wgu, wd;  // within a layer
@@ -65,18 +74,19 @@ KIE_HD PackLayout pack_layout(const Dims& m) {
   PackLayout p{};
   uint64_t o = 0;
   const uint64_t d = m.d, qd = (uint64_t)m.H * m.hd, kvd = (uint64_t)m.Hkv * m.hd, F = m.F;
+  const uint64_t sd = row_stride(m.d), sq = row_stride(m.H * m.hd), sf = row_stride(m.F);
   p.attn_norm = o; o = align_up(o + d, A);
-  p.wqkv = o; o = align_up(o + (qd + 2 * kvd) * d, A);
-  p.wo = o; o = align_up(o + d * qd, A);
+  p.wqkv = o; o = align_up(o + (qd + 2 * kvd) * sd, A);
+  p.wo = o; o = align_up(o + d * sq, A);
   p.mlp_norm = o; o = align_up(o + d, A);
-  p.wgu = o; o = align_up(o + 2 * F * d, A);
-  p.wd = o; o = align_up(o + d * F, A);
+  p.wgu = o; o = align_up(o + 2 * F * sd, A);
+  p.wd = o; o = align_up(o + d * sf, A);
   p.layer_stride = o;
   o = p.layer_stride * (uint64_t)m.L;
   p.final_norm = o; o = align_up(o + d, A);
-  p.lm_head = o; o = align_up(o + (uint64_t)m.V * d, A);
+  p.lm_head = o; o = align_up(o + (uint64_t)m.V * sd, A);
   p.embed = o; o = align_up(o + (uint64_t)m.V * d, A);
-  p.total = o;
+  p.total = o + kBlock;
   return p;
 }
 
@@ -138,11 +148,13 @@ KIE_HD WsLayout ws_layout(const Dims& m, int nwg) {
   return w;
 }
 
-// KV cache: K[l][g][t][hd] then V[l][g][t][hd], fp16
+// KV cache: K[l][g][t][hd] then V[l][g][t][hd], fp16, then kBlock elements
+// of slack (a chunk of keys that runs past the last row stays in the buffer)
 KIE_HD uint64_t kv_offset(const Dims& m, int l, int kv, int g) {
   return (((uint64_t)l * 2 + kv) * m.Hkv + g) * (uint64_t)m.max_ctx * m.hd;
 }
 KIE_HD uint64_t kv_elems(const Dims& m) { return (uint64_t)m.L * 2 * m.Hkv * (uint64_t)m.max_ctx * m.hd; }
+KIE_HD uint64_t kv_alloc_elems(const Dims& m) { return kv_elems(m) + kBlock; }
 
 // ---------------------------------------------------------------------------
 // partitions
@@ -171,6 +183,7 @@ KIE_HD GemvShape gemv_shape(const Dims& m, int kind) {
   }
 }
 KIE_HD int blocks_per_row(int K) { return (K + kBlock - 1) / kBlock; }
+KIE_HD int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 // rows [r0, r1) of op `kind` owned by workgroup wg
 KIE_HD void gemv_rows(const Dims& m, int kind, int nwg, int wg, int* r0, int* r1) {
@@ -181,10 +194,12 @@ KIE_HD void gemv_rows(const Dims& m, int kind, int nwg, int wg, int* r0, int* r1
   *r1 = b * s.unit_rows;
 }
 
-// the workgroup's rows are cut into units (row, 512-column block); wave w
-// takes units [u0, u1) in row-major order
-KIE_HD void gemv_wave_units(int nrows, int K, int wave, int* u0, int* u1) {
-  split(nrows * blocks_per_row(K), kWaves, wave, u0, u1);
+// The workgroup's rows are one contiguous stretch of nrows * row_stride(K)
+// packed elements, read as 1-KB chunks (the last one may run past the end);
+// wave w takes chunks [c0, c1).  A chunk meets at most two rows.
+KIE_HD int gemv_chunks(int nrows, int K) { return ceil_div(nrows * row_stride(K), kBlock); }
+KIE_HD void gemv_wave_chunks(int nrows, int K, int wave, int* c0, int* c1) {
+  split(gemv_chunks(nrows, K), kWaves, wave, c0, c1);
 }
 
 // attention: the n_ctx keys of every KV head are laid end to end
@@ -222,23 +237,25 @@ KIE_HD int attn_kpl(int hd) { return kWave / (hd / 8); }
 
 // per-wave work descriptors kept in LDS (ints):
 //   GEMV kind k (0 QKV, 1 O, 2 GU, 3 DOWN, 4 LM): 8 ints at wave*kWaveDesc + 8k
-//     {offset lo, offset hi (elements from the layer base), b0, n, nb, K8, row0, 0}
-//   attention: 12 ints for the load cursor's step at wave*kWaveDesc + 40 and
-//     12 for the consumer's step at wave*kWaveDesc + 52 (the cursor can be a
-//     step ahead): {g0, ka0, kc0, nst0, pos0, g1, ka1, kc1, nst1, pos1, nseg, merge_g}
+//     {offset lo, offset hi (elements from the layer base to the wave's first
+//      chunk), chunks, first row, first column, row stride, 0, 0}
+//   attention (this step): 12 ints at wave*kWaveDesc + 52
+//     {g0, ka0, kc0, nst0, pos0, g1, ka1, kc1, nst1, pos1, nseg, merge_g}
 //   workgroup rows per GEMV kind: 2 ints at kWaves*kWaveDesc + 2k {r0, nrows}
 constexpr int kWaveDesc = 64;
-constexpr int kCursorAttn = 40;
 constexpr int kConsumerAttn = 52;
 constexpr int kDescInts = kWaves * kWaveDesc + 16;
-// the kernel's non-ring LDS is one static array of this many floats; a model
-// whose LdsPlan needs more is rejected by the host (the ring adds
-// kWaves x kRingDepth KB)
-constexpr int kMainFloats = 23552;
 #ifndef KIE_RING_DEPTH
 #define KIE_RING_DEPTH 8
 #endif
 constexpr int kRingDepth = KIE_RING_DEPTH;
+// LDS of one workgroup: the ring (kWaves x depth KB), a small block of
+// shared scalars, and one static array of main_floats(depth) floats for
+// everything else; a model whose LdsPlan needs more is rejected by the host
+constexpr int kLdsBytes = 160 * 1024;
+constexpr int kSharedReserve = 256;
+KIE_HD constexpr int main_floats(int depth) { return (kLdsBytes - depth * kWaves * kChunkBytes - kSharedReserve) / 4; }
+constexpr int kMainFloats = main_floats(kRingDepth);
 
 // LDS plan (in floats)
 struct LdsPlan {
@@ -249,7 +266,9 @@ struct LdsPlan {
 KIE_HD int imax(int a, int b) { return a > b ? a : b; }
 KIE_HD LdsPlan lds_plan(const Dims& m, int nwg) {
   LdsPlan p{};
-  int kmax = imax(imax(imax(m.d, m.H * m.hd), m.F), 2 * nwg);
+  // GEMV input: two planes of kmax/2 floats (elements 8g..8g+3 at plane 0,
+  // 8g+4..8g+7 at plane 1, position 4g), covering row_stride(K) elements
+  int kmax = imax(imax(imax(row_stride(m.d), row_stride(m.H * m.hd)), row_stride(m.F)), 2 * nwg);
   kmax = (int)align_up((uint64_t)kmax, kBlock);
   int rmax = 0;
   for (int k = 0; k <= PH_LM; ++k) {

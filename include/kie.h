@@ -148,7 +148,10 @@ kie_status kie_decode(kie_ctx* ctx, int32_t n_tokens, int32_t* d_tokens_out, con
 kie_status kie_set_position(kie_ctx* ctx, int32_t pos, int32_t next_token, void* stream);
 
 /* Synchronise `stream` and report errors latched by the kernel
- * (KIE_ERR_TIMEOUT, KIE_ERR_BAD_TOKEN), clearing them. */
+ * (KIE_ERR_TIMEOUT, KIE_ERR_BAD_TOKEN), clearing them.  After such an error
+ * the workspace's exchange state is reset (a timed-out launch can stop in the
+ * middle of a step); the KV cache and the position are kept, so a caller can
+ * rewind with kie_set_position and decode again. */
 kie_status kie_sync_status(kie_ctx* ctx, void* stream);
 
 /* Longest time one wait inside the kernel may take before the launch gives

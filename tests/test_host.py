@@ -60,9 +60,13 @@ def test_unsupported_shapes_rejected():
 def test_sizes_follow_layout():
     for cfg in (CFG0, CFG2, CFG4):
         packed, kvb, ws = kie.query_sizes(cfg)
-        params = cfg.param_elems() * 2
-        assert params <= packed <= params + 4096 * (9 * cfg.n_layers + 3)
-        assert kvb == cfg.n_layers * 2 * cfg.n_kv_heads * cfg.max_ctx * cfg.head_dim * 2
+        off = _offsets(cfg)
+        assert packed == (off["embed"] + cfg.vocab * cfg.d_model + 127) // 128 * 256 + 1024
+        if min(cfg.d_model, cfg.q_dim, cfg.ffn_dim) >= 512:
+            params = cfg.param_elems() * 2
+            assert params <= packed <= params + 4096 * (9 * cfg.n_layers + 3)
+        # the cache itself, then one 1-KB chunk of slack
+        assert kvb == cfg.n_layers * 2 * cfg.n_kv_heads * cfg.max_ctx * cfg.head_dim * 2 + 1024
         assert ws > cfg.max_ctx * cfg.head_dim * 4  # holds the RoPE table
 
 
@@ -84,6 +88,15 @@ def test_host_only_context_refuses_gpu_calls():
         L.kie_destroy(ctx)
 
 
+def _rs(k):
+    """row stride of a packed matrix with k columns: k, or 512 when k < 512"""
+    return max(k, 512)
+
+
+def _mat(flat, rows, k):
+    return flat[: rows * _rs(k)].reshape(rows, _rs(k))[:, :k]
+
+
 def _unpack(cfg: ModelConfig, packed: np.ndarray, offsets):
     """invert the packed layout with the layout rules written out here"""
     d, H, Hkv, hd, F = cfg.d_model, cfg.n_heads, cfg.n_kv_heads, cfg.head_dim, cfg.ffn_dim
@@ -93,7 +106,7 @@ def _unpack(cfg: ModelConfig, packed: np.ndarray, offsets):
         base = l * stride
         g = lambda off, n: packed[base + off: base + off + n]
         out[f"layers.{l}.attn_norm"] = g(offsets["attn_norm"], d)
-        qkv = g(offsets["wqkv"], (H + 2 * Hkv) * hd * d).reshape(-1, d)
+        qkv = _mat(g(offsets["wqkv"], (H + 2 * Hkv) * hd * _rs(d)), (H + 2 * Hkv) * hd, d)
         def unperm(block, heads):
             blk = block.reshape(heads, hd, d)
             o = np.empty_like(blk)
@@ -103,14 +116,14 @@ def _unpack(cfg: ModelConfig, packed: np.ndarray, offsets):
         out[f"layers.{l}.wq"] = unperm(qkv[: H * hd], H)
         out[f"layers.{l}.wk"] = unperm(qkv[H * hd: (H + Hkv) * hd], Hkv)
         out[f"layers.{l}.wv"] = qkv[(H + Hkv) * hd:]
-        out[f"layers.{l}.wo"] = g(offsets["wo"], d * H * hd).reshape(d, H * hd)
+        out[f"layers.{l}.wo"] = _mat(g(offsets["wo"], d * _rs(H * hd)), d, H * hd)
         out[f"layers.{l}.mlp_norm"] = g(offsets["mlp_norm"], d)
-        gu = g(offsets["wgu"], 2 * F * d).reshape(2 * F, d)
+        gu = _mat(g(offsets["wgu"], 2 * F * _rs(d)), 2 * F, d)
         out[f"layers.{l}.w_gate"] = gu[0::2]
         out[f"layers.{l}.w_up"] = gu[1::2]
-        out[f"layers.{l}.w_down"] = g(offsets["wd"], d * F).reshape(d, F)
+        out[f"layers.{l}.w_down"] = _mat(g(offsets["wd"], d * _rs(F)), d, F)
     out["final_norm"] = packed[offsets["final_norm"]: offsets["final_norm"] + d]
-    out["lm_head"] = packed[offsets["lm_head"]: offsets["lm_head"] + cfg.vocab * d].reshape(cfg.vocab, d)
+    out["lm_head"] = _mat(packed[offsets["lm_head"]:], cfg.vocab, d)
     out["embed"] = packed[offsets["embed"]: offsets["embed"] + cfg.vocab * d].reshape(cfg.vocab, d)
     return out
 
@@ -122,15 +135,15 @@ def _offsets(cfg):
     o = {}
     x = 0
     o["attn_norm"] = x; x = a(x + d)
-    o["wqkv"] = x; x = a(x + (qd + 2 * kvd) * d)
-    o["wo"] = x; x = a(x + d * qd)
+    o["wqkv"] = x; x = a(x + (qd + 2 * kvd) * _rs(d))
+    o["wo"] = x; x = a(x + d * _rs(qd))
     o["mlp_norm"] = x; x = a(x + d)
-    o["wgu"] = x; x = a(x + 2 * F * d)
-    o["wd"] = x; x = a(x + d * F)
+    o["wgu"] = x; x = a(x + 2 * F * _rs(d))
+    o["wd"] = x; x = a(x + d * _rs(F))
     o["layer_stride"] = x
     x = x * cfg.n_layers
     o["final_norm"] = x; x = a(x + d)
-    o["lm_head"] = x; x = a(x + cfg.vocab * d)
+    o["lm_head"] = x; x = a(x + cfg.vocab * _rs(d))
     o["embed"] = x
     return o
 
@@ -153,6 +166,12 @@ def test_packer_is_a_permutation(cfg):
     back = _unpack(cfg, packed, off)
     for k, v in w.items():
         assert np.array_equal(back[k], v.view(np.uint16)), k
+    # the kernel streams whole 1-KB chunks: row pads and the tail slack are zeros
+    assert not packed[-512:].any()
+    d, rows = cfg.d_model, (cfg.n_heads + 2 * cfg.n_kv_heads) * cfg.head_dim
+    if _rs(d) > d:
+        qkv = packed[off["wqkv"]: off["wqkv"] + rows * _rs(d)].reshape(rows, _rs(d))
+        assert not qkv[:, d:].any()
 
 
 @needs_lib
