@@ -576,8 +576,10 @@ struct GemvAcc {
       A = t;
       S += kBlock;
     } else {
-      // row R ends in this chunk (lanes past its end already hold row R + 1)
-      const float sum = wave_sum(inR ? t : 0.f);
+      // Row R ends in this chunk.  A lane still in row R finishes it with t;
+      // a lane past the end starts row R + 1 with t, and its earlier chunks
+      // of row R are in A.
+      const float sum = wave_sum(inR ? t : A);
       if (lane == 0) part[R * kWaves + wave] = sum;
       A = inR ? 0.f : t;
       ++R;

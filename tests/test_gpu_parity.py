@@ -79,6 +79,9 @@ def test_many_keys_per_wave(hd, H, d):
     dict(n_heads=8, n_kv_heads=4, head_dim=32, name="gqa2"),
     dict(d_model=320, n_heads=4, n_kv_heads=4, head_dim=80, ffn_dim=864, name="hd80"),
     dict(d_model=384, n_heads=6, n_kv_heads=6, head_dim=64, ffn_dim=1536, vocab=1000, name="ragged"),
+    # rows of 864 and 1000 columns: 1-KB chunks straddle row ends in the
+    # middle of a wave's range in every GEMV (several rows per workgroup)
+    dict(d_model=864, n_heads=4, n_kv_heads=2, head_dim=64, ffn_dim=1000, vocab=3000, name="straddle"),
 ], ids=lambda s: s["name"])
 def test_small_shapes_teacher_forced(shape):
     cfg = CFG0.with_(seed_index=11, prompt_len=9, decode_steps=12, **shape)
