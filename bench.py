@@ -16,6 +16,8 @@ decode step on the host for a bounded sample.
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
 import hashlib
 import json
 import os
@@ -39,9 +41,9 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(cfg_name: str):
+def measured_traffic(cfg_name: str, prompt: int, steps: int):
     """HBM bytes per launch from the committed rocprofv3 --pmc summary, only
-    if it was taken on the kernel source as it is now"""
+    if it was taken on the kernel source as it is now, for the same run"""
     p = os.path.join(ROOT, "profiles", f"traffic_{cfg_name}.json")
     if not os.path.exists(p):
         return None
@@ -51,7 +53,20 @@ def measured_traffic(cfg_name: str):
         return None
     if d.get("kernel_source_hash") != kernel_source_hash():
         return None
+    if d.get("prompt") != prompt or d.get("decode_steps") != steps:
+        return None
     return d.get("hbm_bytes_per_launch")
+
+
+def blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        n = [d.get("num_threads", 0) for d in threadpool_info() if d.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
+    except Exception:
+        pass
+    return int(os.environ.get("OPENBLAS_NUM_THREADS") or os.environ.get("OMP_NUM_THREADS") or os.cpu_count())
 
 
 def cpu_baseline(cfg, weights, pos: int, n_steps: int):
@@ -71,10 +86,73 @@ def cpu_baseline(cfg, weights, pos: int, n_steps: int):
         lg = orc.step(cache, tok, pos + 1 + k)
         tok = int(np.argmax(lg))
     dt = time.perf_counter() - t0
-    threads = os.environ.get("OPENBLAS_NUM_THREADS") or os.environ.get("OMP_NUM_THREADS") or str(os.cpu_count())
-    return dict(value=n_steps / dt, unit="tok/s", cores=int(threads), kind="oracle",
+    return dict(value=round(n_steps / dt, 3), unit="tok/s", cores=blas_threads(), kind="oracle",
                 sample=f"{n_steps} fp64 oracle decode steps of {cfg.name} at context {pos + 1}..{pos + n_steps} "
                        f"(random fp64 KV cache in place of the prompt; weight upcast not timed)")
+
+
+# ---------------------------------------------------------------------------
+# rocprofv3 summaries (written under profiles/; the commands are in them)
+# ---------------------------------------------------------------------------
+def _rows(d, suffix):
+    fs = sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True))
+    if not fs:
+        raise SystemExit(f"no *{suffix} under {d}")
+    with open(fs[0]) as fh:
+        return list(csv.DictReader(fh))
+
+
+def summarize_trace(d: str, command: str) -> str:
+    """markdown: per-kernel stats and every monokernel dispatch"""
+    stats = _rows(d, "kernel_stats.csv")
+    trace = _rows(d, "kernel_trace.csv")
+    out = ["# rocprofv3 kernel trace of the default benchmark run (cfg2, 2048-token prompt, 512 decode steps)", "",
+           "Command (from the repository root on the GPU box):", "", "```", command, "```", "",
+           "| kernel | calls | total ms | average ms | min ms | max ms |", "|---|---|---|---|---|---|"]
+    for r in stats:
+        ns = lambda k: float(r[k]) / 1e6
+        out.append(f"| `{r['Name'][:70]}` | {r['Calls']} | {ns('TotalDurationNs'):.3f} | {ns('AverageNs'):.3f} | "
+                   f"{ns('MinNs'):.3f} | {ns('MaxNs'):.3f} |")
+    mk = [r for r in trace if "kie_monokernel" in r["Kernel_Name"]]
+    out += ["", "Every launch of the persistent kernel, in order: the prompt's launches, the warm-up decode, "
+            "then the timed decode (the last row; bench.py's HIP events time the same launch).", "",
+            "| # | duration ms |", "|---|---|"]
+    for i, r in enumerate(mk):
+        out.append(f"| {i} | {(int(r['End_Timestamp']) - int(r['Start_Timestamp'])) / 1e6:.3f} |")
+    return "\n".join(out) + "\n"
+
+
+def summarize_traffic(fetch_dir: str, write_dir: str, copy_bytes: int, cfg_name: str, steps: int,
+                      prompt: int) -> dict:
+    """HBM bytes of the timed decode launch from FETCH_SIZE / WRITE_SIZE (KiB
+    per dispatch), each scaled by what it reads for a plain copy of
+    copy_bytes (read copy_bytes, write copy_bytes)"""
+    def pick(d, counter):
+        rows = [r for r in _rows(d, "counter_collection.csv") if r["Counter_Name"] == counter]
+        mono = [r for r in rows if "kie_monokernel" in r["Kernel_Name"]]
+        last_mono = max(int(r["Dispatch_Id"]) for r in mono) if mono else 0
+        copies = [r for r in rows if int(r["Dispatch_Id"]) > last_mono]
+        if not mono or not copies:
+            raise SystemExit(f"{counter}: missing dispatches in {d}")
+        timed = max(mono, key=lambda r: int(r["Dispatch_Id"]))
+        copy = max(copies, key=lambda r: int(r["Dispatch_Id"]))  # the multiply that copies
+        return float(timed["Counter_Value"]) * 1024.0, float(copy["Counter_Value"]) * 1024.0, copy["Kernel_Name"]
+    f_k, f_c, f_name = pick(fetch_dir, "FETCH_SIZE")
+    w_k, w_c, _ = pick(write_dir, "WRITE_SIZE")
+    sf, sw = copy_bytes / f_c, copy_bytes / w_c
+    from decode_persistent_monokernel_amd.config import preset
+    algo = preset(cfg_name).run_bytes(prompt, steps)
+    return {
+        "config": cfg_name, "prompt": prompt, "decode_steps": steps,
+        "kernel_source_hash": kernel_source_hash(),
+        "fetch_kib_raw": f_k / 1024, "write_kib_raw": w_k / 1024,
+        "copy_kernel": f_name[:80], "copy_bytes": copy_bytes,
+        "fetch_scale": sf, "write_scale": sw,
+        "hbm_read_bytes_per_launch": f_k * sf, "hbm_write_bytes_per_launch": w_k * sw,
+        "hbm_bytes_per_launch": f_k * sf + w_k * sw,
+        "algorithmic_bytes_per_launch": algo,
+        "ratio_to_algorithmic": (f_k * sf + w_k * sw) / algo,
+    }
 
 
 def main():
@@ -87,7 +165,28 @@ def main():
     ap.add_argument("--cpu-steps", type=int, default=24)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--repeats", type=int, default=0, help="extra timed repeats for the launch-time spread")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="after the timed decode, run one plain device copy of this many bytes (the reference "
+                         "dispatch for scaling HBM counters)")
+    ap.add_argument("--summarize-trace", metavar="DIR", help="write a markdown summary of a rocprofv3 "
+                    "--kernel-trace --stats output directory to stdout and exit")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="print the JSON traffic summary of two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) "
+                         "of this command with --copy-bytes and exit")
+    ap.add_argument("--command", default="", help="the profiled command, recorded in a summary")
     args = ap.parse_args()
+
+    if args.summarize_trace:
+        sys.stdout.write(summarize_trace(args.summarize_trace, args.command))
+        return
+    if args.summarize_traffic:
+        from decode_persistent_monokernel_amd.config import preset
+        P = args.prompt if args.prompt is not None else preset(args.config).prompt_len
+        res = summarize_traffic(args.summarize_traffic[0], args.summarize_traffic[1], args.copy_bytes,
+                                args.config, args.steps, P)
+        res["command"] = args.command
+        print(json.dumps(res, indent=1))
+        return
 
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -149,7 +248,7 @@ def main():
     n_launches = (K + max(K, W, 1) - 1) // max(K, W, 1)
     algo_bytes = cfg.run_bytes(P, K)
     achieved = algo_bytes / (kernel_ms * 1e-3) / 1e9
-    traffic = measured_traffic(cfg.name)
+    traffic = measured_traffic(cfg.name, P, K)
     value = K / wall
     res = {
         "metric": METRIC,
@@ -189,6 +288,13 @@ def main():
     }
     eng.close()
     del eng
+    if args.copy_bytes > 0:
+        src = torch.ones(args.copy_bytes // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.mul(src, 1.0, out=dst)  # an elementwise kernel: reads and writes copy_bytes
+        torch.cuda.synchronize()
+        del src, dst
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, w, P, args.cpu_steps)
     print(json.dumps(res), flush=True)
