@@ -253,7 +253,39 @@ KIE_DI bool poll_words(const Dev& D, const u64* base, int stride, uint32_t mask,
   }
 }
 
-// the workgroup polls words [0, n) of src into dst (swizzled for GEMV input)
+// Wait until the words *a[k] (k < N, mask bit k set) all carry `epoch`, as
+// poll_words for scattered addresses.  Returns false on timeout or abort.
+template <int N>
+KIE_DI bool poll_addrs(const Dev& D, const u64* const (&a)[N], uint32_t mask, uint32_t epoch, u64 (&v)[N]) {
+#pragma unroll
+  for (int k = 0; k < N; ++k)
+    if (mask & (1u << k)) v[k] = ll_load(a[k]);
+  uint64_t t0 = 0;
+  for (int it = 0;; ++it) {
+    uint32_t stale = 0;
+#pragma unroll
+    for (int k = 0; k < N; ++k)
+      if ((mask & (1u << k)) && ll_epoch(v[k]) != epoch) stale |= 1u << k;
+    if (!stale) return true;
+    if (it == 0) t0 = wall_clock64();
+    if ((it & 15) == 15) {
+      if (*(volatile int*)&D.sh->abort) return false;
+      if (__hip_atomic_load(&D.state[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+        D.sh->abort = 1;
+        return false;
+      }
+      if (wall_clock64() - t0 > D.p->timeout_ticks) {
+        raise_status(D, DEV_TIMEOUT);
+        return false;
+      }
+    }
+    __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+    for (int k = 0; k < N; ++k)
+      if (stale & (1u << k)) v[k] = ll_load(a[k]);
+  }
+}
+
 // the workgroup polls words [0, n) of src into dst (planes for a GEMV input)
 template <bool SWZ>
 KIE_DI void poll_to_lds(const Dev& D, const u64* src, float* dst, int n, uint32_t epoch) {
@@ -883,8 +915,39 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
         // ================= attention over the KV cache ==================
         float mrow[G], lrow[G], acc[G][8], q[G][8];
         const int nseg = rfl(adesc[10]);
+        // The query heads of every segment and the key and value at the
+        // current position (all written by this step's QKV epilogue), polled
+        // once by the whole workgroup into LDS: qkv[sg][G + 2][hd].  No wave
+        // then waits on a remote word between or after its streams.
+        float* qkv = lds_dyn + p.lp.attn_qkv;
+        {
+          const int per = (G + 2) * hd;
+          const int g0 = rfl(adesc[0]), g1 = rfl(adesc[5]);
+          for (int base = D.tid; base < nseg * per; base += kThreads * 8) {
+            const u64* a[8];
+            uint32_t mask = 0;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+              const int i = base + k * kThreads;
+              a[k] = D.Q;
+              if (i < nseg * per) {
+                const int sg = i / per, j = i % per, row = j / hd, dd = j % hd;
+                const int g = sg ? g1 : g0;
+                a[k] = row < G ? D.Q + (uint64_t)l * qd + (uint64_t)(g * G + row) * hd + dd
+                               : (row == G ? D.KC : D.VC) + (uint64_t)l * kvd + (uint64_t)g * hd + dd;
+                mask |= 1u << k;
+              }
+            }
+            u64 v[8];
+            if (!poll_addrs<8>(D, a, mask, epoch, v)) break;
+#pragma unroll
+            for (int k = 0; k < 8; ++k)
+              if (mask & (1u << k)) qkv[base + k * kThreads] = ll_f(v[k]);
+          }
+        }
+        wg_sync();
+        if (aborted(D)) { __builtin_amdgcn_s_waitcnt(kWaitAllVm); return; }
         for (int sg = 0; sg < nseg; ++sg) {
-          const int g = rfl(adesc[5 * sg + 0]);
           const int ka = rfl(adesc[5 * sg + 1]), kc = rfl(adesc[5 * sg + 2]), nst = rfl(adesc[5 * sg + 3]);
           const int has_pos = rfl(adesc[5 * sg + 4]);
 #pragma unroll
@@ -895,29 +958,19 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
             for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
           }
           // this lane's 8 query dims of every head in the group
-          {
-            const u64* qb = D.Q + (uint64_t)l * qd + (uint64_t)g * G * hd + D.dl * 8;
+          const float* qs = qkv + sg * (G + 2) * hd + D.dl * 8;
 #pragma unroll
-            for (int h = 0; h < G; ++h) {
-              u64 qw[8];
-              poll_words<8>(D, qb + h * hd, 1, 0xFFu, epoch, qw);
+          for (int h = 0; h < G; ++h)
 #pragma unroll
-              for (int e = 0; e < 8; ++e) q[h][e] = ll_f(qw[e]);
-            }
-          }
+            for (int e = 0; e < 8; ++e) q[h][e] = qs[h * hd + e];
           attn_stream<G>(D, cur, slot, nst, ka, kc, q, mrow, lrow, acc);
           if (has_pos) {
-            // current key and value (fp16-rounded) from the QKV epilogue
-            const u64* kp = D.KC + (uint64_t)l * kvd + (uint64_t)g * hd + D.dl * 8;
-            const u64* vp = D.VC + (uint64_t)l * kvd + (uint64_t)g * hd + D.dl * 8;
-            u64 kw[8], vw[8];
+            // current key and value (fp16-rounded by the QKV epilogue)
             float kx[8], vx[8];
-            poll_words<8>(D, kp, 1, 0xFFu, epoch, kw);
-            poll_words<8>(D, vp, 1, 0xFFu, epoch, vw);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-              kx[e] = ll_f(kw[e]);
-              vx[e] = ll_f(vw[e]);
+              kx[e] = qs[G * hd + e];
+              vx[e] = qs[(G + 1) * hd + e];
             }
             const bool mine = D.lane < D.lpk;
 #pragma unroll

@@ -259,7 +259,7 @@ constexpr int kMainFloats = main_floats(kRingDepth);
 
 // LDS plan (in floats)
 struct LdsPlan {
-  int xraw, big, gemv_xs, gemv_part, attn_wrec, attn_ml, own, desc;
+  int xraw, big, gemv_xs, gemv_part, attn_wrec, attn_ml, attn_qkv, own, desc;
   int total_floats;
   int kmax, rmax, max_recs;
 };
@@ -290,11 +290,13 @@ KIE_HD LdsPlan lds_plan(const Dims& m, int nwg) {
   const int gemv_sz = kmax + (int)align_up((uint64_t)rmax * kWaves, 64);
   // attention: per-wave records (2 segments x kWaves), later reused by the
   // merger for the records of every workgroup that met its head, then
-  // 4 floats per record
+  // 4 floats per record, then per segment the G query heads and the key and
+  // value at the current position
   const int wrec_sz = imax(2 * kWaves * m.G * (m.hd + 2), max_recs * m.G * (m.hd + 2));
   p.attn_wrec = o;
   p.attn_ml = o + wrec_sz;
-  const int attn_sz = wrec_sz + max_recs * 4;
+  p.attn_qkv = p.attn_ml + max_recs * 4;
+  const int attn_sz = wrec_sz + max_recs * 4 + 2 * (m.G + 2) * m.hd;
   o += (int)align_up((uint64_t)imax(gemv_sz, attn_sz), 64);
   p.own = o; o += (int)align_up((uint64_t)2 * ((m.d + nwg - 1) / nwg), 64);
   p.desc = o; o += kDescInts;
