@@ -115,6 +115,13 @@ KIE_DI int xs_pos(int k, int plane) { return ((k >> 2) & 1) * plane + ((k >> 3) 
 // one, and a loop with a possibly divergent exit makes all its loop-carried
 // state (the load cursor, the ring slot) per-lane vector values.
 KIE_DI int rfl(int v) { return __builtin_amdgcn_readfirstlane(v); }
+// A per-lane value the compiler must treat as new at every use: index math
+// built on it stays inside the loop that needs it instead of being hoisted to
+// the kernel entry, where it would hold registers for the whole launch.
+KIE_DI int opaque(int v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
 
 // combine (m, l, acc) with (mo, lo, ao); m in log2 units, -inf = empty
 KIE_DI void lse_merge(float& m, float& l, float* acc, float mo, float lo, const float* ao) {
@@ -175,6 +182,7 @@ struct Dev {
   int32_t* state;
   u64 *X, *Q, *KC, *VC, *REC, *OB, *HB, *LMP;
   const float2* rope;
+  uint32_t* tbuf;     // LDS phase stamps of the current step (tracing only)
   int lpk, kpl, kl, dl, lane_active;
 };
 
@@ -211,11 +219,46 @@ KIE_DI bool spin_word(const Dev& D, const u64* a, uint32_t epoch, u64* out) {
   }
 }
 
-// phase trace stamp (thread 0 of the workgroup only)
+// Phase trace stamp (thread 0 of the workgroup only).  Stamps go to LDS and
+// reach memory at the end of the step: a global store here would be waited
+// for by the next vmcnt wait of the wave and move the very times measured.
+KIE_DI bool tracing(const Dev& D, int s) { return D.p->trace && s < D.p->trace_steps; }
 KIE_DI void stamp(const Dev& D, int s, int ph, int k) {
-  const KParams& p = *D.p;
-  if (p.trace && s < p.trace_steps && D.tid == 0)
-    p.trace[(((uint64_t)s * kTracePhases + ph) * D.nwg + D.wg) * 4 + k] = wall_clock64();
+  if (tracing(D, s) && D.tid == 0) {
+    if (!D.tbuf) {  // no room in LDS
+      D.p->trace[(((uint64_t)s * kTracePhases + ph) * D.nwg + D.wg) * 4 + k] = wall_clock64();
+      return;
+    }
+    const int L = D.p->m.L;
+    const int slot = ph < 5 * 64 ? ph : trace_slots(L) - 1;
+    D.tbuf[slot * 4 + k] = (uint32_t)wall_clock64();
+  }
+}
+// (every thread) clear the step's stamps
+KIE_DI void trace_begin(const Dev& D, int s) {
+  if (!tracing(D, s) || !D.tbuf) return;
+  const int n = trace_slots(D.p->m.L) * 4;
+  for (int i = D.tid; i < n; i += kThreads) D.tbuf[i] = 0;
+}
+// (every thread) write the step's stamps to the trace buffer, widened to 64
+// bits against the current clock; holds one workgroup barrier
+KIE_DI void trace_end(const Dev& D, int s) {
+  if (!tracing(D, s) || !D.tbuf) return;
+  const int L = D.p->m.L;
+  const int n = trace_slots(L) * 4;
+  const uint64_t now = wall_clock64();
+  for (int i = D.tid; i < n; i += kThreads) {
+    const uint32_t lo = D.tbuf[i];
+    uint64_t v = 0;
+    if (lo) {
+      v = (now & ~0xFFFFFFFFull) | lo;
+      if (v > now) v -= 1ull << 32;
+    }
+    const int slot = i >> 2;
+    const int ph = slot < trace_slots(L) - 1 ? slot : 5 * 64 + 1;
+    D.p->trace[(((uint64_t)s * kTracePhases + ph) * D.nwg + D.wg) * 4 + (i & 3)] = v;
+  }
+  wg_sync();
 }
 
 // Wait until the words base[k*stride] (k < N, mask bit k set) all carry
@@ -723,20 +766,25 @@ KIE_DI void attn_stream(const Dev& D, Cursor& cur, int& slot, int nst, int ka, i
 // ---------------------------------------------------------------------------
 // prologue helpers
 // ---------------------------------------------------------------------------
-// xraw -> xs = g * x / sqrt(mean(x^2) + eps), swizzled, zero tail to nb*512
 // this thread's RMSNorm gains (elements tid + k * kThreads), loaded into
-// registers before the input is polled so that their latency overlaps it
-KIE_DI void load_gains(const Dev& D, const uint16_t* g, float (&gr)[kGainRegs]) {
+// registers before the input is polled so that their latency overlaps it.
+// The loads are unconditional (a clamped index) and the raw half bits stay
+// unconverted until use: a load whose value is used inside its own branch
+// gets a wait for it right there, and the loads would run one at a time.
+KIE_DI void load_gains(const Dev& D, const uint16_t* g, uint16_t (&gr)[kGainRegs]) {
   const int d = D.p->m.d;
+  const int t = opaque(D.tid);
 #pragma unroll
   for (int k = 0; k < kGainRegs; ++k) {
-    const int i = D.tid + k * kThreads;
-    gr[k] = i < d ? hbits2f(g[i]) : 0.f;
+    const int i = t + k * kThreads;
+    gr[k] = g[i < d ? i : 0];
   }
   asm volatile("" ::: "memory");  // issue the loads here, ahead of the poll
 }
 
-KIE_DI void rmsnorm_to_xs(const Dev& D, const float* xraw, const float (&gr)[kGainRegs], float* xs) {
+// xraw -> xs = g * x / sqrt(mean(x^2) + eps) in the two-plane layout, zero
+// up to the padded row length
+KIE_DI void rmsnorm_to_xs(const Dev& D, const float* xraw, const uint16_t (&gr)[kGainRegs], float* xs) {
   const KParams& p = *D.p;
   const int d = p.m.d;
   float ss = 0.f;
@@ -752,7 +800,7 @@ KIE_DI void rmsnorm_to_xs(const Dev& D, const float* xraw, const float (&gr)[kGa
 #pragma unroll
   for (int k = 0; k < kGainRegs; ++k) {
     const int i = D.tid + k * kThreads;
-    if (i < padded) xs[xs_pos(i, D.plane)] = i < d ? xraw[i] * inv * gr[k] : 0.f;
+    if (i < padded) xs[xs_pos(i, D.plane)] = i < d ? xraw[i] * inv * hbits2f(gr[k]) : 0.f;
   }
 }
 
@@ -798,6 +846,7 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
   D.HB = (u64*)(p.ws + p.wl.HB);
   D.LMP = (u64*)(p.ws + p.wl.LMP);
   D.rope = (const float2*)(p.ws + p.wl.rope);
+  D.tbuf = p.lp.trace >= 0 ? (uint32_t*)(lds_dyn + p.lp.trace) : nullptr;
   D.lpk = attn_lpk(p.m.hd);
   D.kpl = attn_kpl(p.m.hd);
   D.kl = D.lane / D.lpk;
@@ -872,6 +921,7 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
 #pragma unroll 1
     for (int i = 0; i < kDepth; ++i) cursor_issue(D, cur, ring_add(slot, i));
 
+    trace_begin(D, s);
     // ---- input token and embedding ------------------------------------
     if (p.forced) {
       token = p.forced[s];
@@ -883,8 +933,20 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
       token = 0;
     }
     {
+      // all loads first, then the conversions (see load_gains)
       const uint16_t* e = p.W + p.pl.embed + (uint64_t)token * d;
-      for (int i = D.tid; i < d; i += kThreads) xraw[i] = hbits2f(e[i]);
+      uint16_t ev[kGainRegs];
+      const int t = opaque(D.tid);
+#pragma unroll
+      for (int k = 0; k < kGainRegs; ++k) {
+        const int i = t + k * kThreads;
+        ev[k] = e[i < d ? i : 0];
+      }
+#pragma unroll
+      for (int k = 0; k < kGainRegs; ++k) {
+        const int i = t + k * kThreads;
+        if (i < d) xraw[i] = hbits2f(ev[k]);
+      }
     }
     wg_sync();
     if (p.m.parallel) {
@@ -1143,17 +1205,17 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
       const int gi = gemv_index(kind);
       const int r0 = rfl(wgrows[2 * gi]), nrows = rfl(wgrows[2 * gi + 1]);
       // prologue: the input vector
-      float gr[kGainRegs];
+      uint16_t gr[kGainRegs];
       float2 rope_cs = make_float2(1.f, 0.f);
       if (kind == PH_QKV) {
         load_gains(D, Wl + p.pl.attn_norm, gr);
         // this thread's RoPE factors for the epilogue, fetched ahead too
-        if (2 * D.tid < nrows) {
+        // (unconditionally, from a clamped index: see load_gains)
+        {
           const int rr = r0 + 2 * D.tid;
-          if (rr < qd + kvd) {
-            const int i = ((rr < qd ? rr : rr - qd) % hd) >> 1;
-            rope_cs = D.rope[(uint64_t)pos * (hd / 2) + i];
-          }
+          const bool mine = 2 * D.tid < nrows && rr < qd + kvd;
+          const int i = mine ? ((rr < qd ? rr : rr - qd) % hd) >> 1 : 0;
+          rope_cs = D.rope[(uint64_t)pos * (hd / 2) + i];
         }
         asm volatile("" ::: "memory");
         if (p.m.parallel ? (l > p.m.delay) : (l > 0)) {
@@ -1381,6 +1443,7 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
       }
     }
     wg_sync();
+    trace_end(D, s);
   }  // steps
   __builtin_amdgcn_s_waitcnt(kWaitAllVm);  // no ring DMA may outlive the workgroup
 }

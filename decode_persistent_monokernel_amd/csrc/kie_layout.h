@@ -257,9 +257,13 @@ constexpr int kSharedReserve = 256;
 KIE_HD constexpr int main_floats(int depth) { return (kLdsBytes - depth * kWaves * kChunkBytes - kSharedReserve) / 4; }
 constexpr int kMainFloats = main_floats(kRingDepth);
 
+// phase slots of one step in the LDS trace buffer: 5 per layer, the LM
+// head, the end of the step
+KIE_HD int trace_slots(int L) { return 5 * L + 2; }
+
 // LDS plan (in floats)
 struct LdsPlan {
-  int xraw, big, gemv_xs, gemv_part, attn_wrec, attn_ml, attn_qkv, own, desc;
+  int xraw, big, gemv_xs, gemv_part, attn_wrec, attn_ml, attn_qkv, own, desc, trace;
   int total_floats;
   int kmax, rmax, max_recs;
 };
@@ -300,6 +304,13 @@ KIE_HD LdsPlan lds_plan(const Dims& m, int nwg) {
   o += (int)align_up((uint64_t)imax(gemv_sz, attn_sz), 64);
   p.own = o; o += (int)align_up((uint64_t)2 * ((m.d + nwg - 1) / nwg), 64);
   p.desc = o; o += kDescInts;
+  // phase trace of one step (32-bit stamps, written out at the step's end),
+  // when it fits; otherwise stamps go straight to memory
+  p.trace = -1;
+  if (o + trace_slots(m.L) * 4 <= kMainFloats) {
+    p.trace = o;
+    o += trace_slots(m.L) * 4;
+  }
   p.total_floats = o;
   return p;
 }
