@@ -514,7 +514,7 @@ kie_status kie_validate_schedule(const kie_model_config* cfg, int32_t nwg, int32
       if (seg[s].tb == n_ctx) mergers[seg[s].g]++;
       for (int wave = 0; wave < kie::kWaves; ++wave) {
         int wa, wb;
-        kie::split(seg[s].tb - seg[s].ta, kie::kWaves, wave, &wa, &wb);
+        kie::wave_split(seg[s].tb - seg[s].ta, wave, &wa, &wb);
         wa += seg[s].ta;
         wb += seg[s].ta;
         for (int t = wa; t < wb; ++t) key_owner[(size_t)seg[s].g * n_ctx + t]++;

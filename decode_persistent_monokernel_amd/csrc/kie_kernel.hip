@@ -397,7 +397,7 @@ KIE_DI void write_attn_desc(const KParams& p, int nwg, int wg, int wave, int kpl
     int ka = 0, kc = 0, nst = 0, hp = 0;
     if (s < nseg) {
       int wa, wb;
-      split(seg[s].tb - seg[s].ta, kWaves, wave, &wa, &wb);
+      wave_split(seg[s].tb - seg[s].ta, wave, &wa, &wb);
       wa += seg[s].ta;
       wb += seg[s].ta;
       ka = wa;

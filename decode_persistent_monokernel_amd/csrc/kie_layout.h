@@ -164,6 +164,19 @@ KIE_HD void split(int n, int parts, int i, int* a, int* b) {
   *a = (int)(((uint32_t)n * (uint32_t)i) / (uint32_t)parts);
   *b = (int)(((uint32_t)n * (uint32_t)(i + 1)) / (uint32_t)parts);
 }
+// Split n items over the kWaves waves of a workgroup in contiguous ranges.
+// Waves w and w + 4 share a SIMD and the older one, w, wins most issue slots
+// while both run, so it gets the larger share: weights (16 + kWaveSkew) and
+// (16 - kWaveSkew) sixteenths, so that both finish together.
+#ifndef KIE_WAVE_SKEW
+#define KIE_WAVE_SKEW 2
+#endif
+constexpr int kWaveSkew = KIE_WAVE_SKEW;
+KIE_HD int wave_cum(int w) { return w <= 4 ? w * (16 + kWaveSkew) : 4 * (16 + kWaveSkew) + (w - 4) * (16 - kWaveSkew); }
+KIE_HD void wave_split(int n, int wave, int* a, int* b) {
+  *a = (int)(((uint64_t)n * (uint64_t)wave_cum(wave)) / (uint64_t)(16 * kWaves));
+  *b = (int)(((uint64_t)n * (uint64_t)wave_cum(wave + 1)) / (uint64_t)(16 * kWaves));
+}
 // the part that holds item f (0 <= f < n) under split()
 KIE_HD int split_owner(int f, int n, int parts) {
   return (int)(((uint32_t)(f + 1) * (uint32_t)parts + (uint32_t)n - 1) / (uint32_t)n) - 1;
@@ -199,7 +212,7 @@ KIE_HD void gemv_rows(const Dims& m, int kind, int nwg, int wg, int* r0, int* r1
 // wave w takes chunks [c0, c1).  A chunk meets at most two rows.
 KIE_HD int gemv_chunks(int nrows, int K) { return ceil_div(nrows * row_stride(K), kBlock); }
 KIE_HD void gemv_wave_chunks(int nrows, int K, int wave, int* c0, int* c1) {
-  split(gemv_chunks(nrows, K), kWaves, wave, c0, c1);
+  wave_split(gemv_chunks(nrows, K), wave, c0, c1);
 }
 
 // attention: the n_ctx keys of every KV head are laid end to end
