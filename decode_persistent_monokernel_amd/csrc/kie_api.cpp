@@ -506,11 +506,9 @@ kie_status kie_validate_schedule(const kie_model_config* cfg, int32_t nwg, int32
   for (int w = 0; w < nwg; ++w) {
     kie::AttnSeg seg[2];
     const int ns = kie::attn_segments(m.Hkv, n_ctx, nwg, w, seg);
-    int fa, fb;
-    kie::split(m.Hkv * n_ctx, nwg, w, &fa, &fb);
-    int covered = 0;
+    if (ns > 1) return bad("a workgroup meets more than one KV head");
     for (int s = 0; s < ns; ++s) {
-      covered += seg[s].tb - seg[s].ta;
+      if (seg[s].g != kie::attn_head(m.Hkv, nwg, w)) return bad("segment outside the workgroup's head");
       if (seg[s].tb == n_ctx) mergers[seg[s].g]++;
       for (int wave = 0; wave < kie::kWaves; ++wave) {
         int wa, wb;
@@ -522,10 +520,10 @@ kie_status kie_validate_schedule(const kie_model_config* cfg, int32_t nwg, int32
         const int nst = (kc - wa + kpl - 1) / kpl;
         if (nst * kpl < kc - wa) return bad("attention steps miss keys");
       }
-      if (kie::attn_owner(m.Hkv, n_ctx, nwg, seg[s].g, seg[s].ta) != w)
+      if (kie::attn_owner(m.Hkv, n_ctx, nwg, seg[s].g, seg[s].ta) != w ||
+          kie::attn_owner(m.Hkv, n_ctx, nwg, seg[s].g, seg[s].tb - 1) != w)
         return bad("attn_owner disagrees with attn_segments");
     }
-    if (covered != fb - fa) return bad("workgroup range meets more than two heads");
   }
   for (int v : key_owner)
     if (v != 1) return bad("attention key covered zero or several times");

@@ -76,6 +76,11 @@ KIE_DI float wave_sum(float v) {
   v = row16_sum(v);
   return (readlane_f(v, 0) + readlane_f(v, 16)) + (readlane_f(v, 32) + readlane_f(v, 48));
 }
+// full-wave maximum (every lane gets it)
+KIE_DI float wave_max(float v) {
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  return v;
+}
 // sum over groups of `lpk` consecutive lanes; every lane of a group gets it
 KIE_DI float group_sum(float v, int lpk) {
   if (lpk == 16) return row16_sum(v);
@@ -1106,13 +1111,13 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
           const int n_ctx = pos + 1;
           const int w_first = attn_owner(Hkv, n_ctx, D.nwg, g, 0);
           const int nrec = D.wg - w_first + 1;
-          // 1. which records exist: mlw[r*4 + 3] = segment of record r or -1
+          // 1. which records exist: mlw[r*8 + 7] = segment of record r or -1
           for (int r = D.tid; r < nrec; r += kThreads) {
             AttnSeg sgs[2];
             sgs[0] = AttnSeg{0, 0, 0};
             sgs[1] = AttnSeg{0, 0, 0};
             const int ns = attn_segments(Hkv, n_ctx, D.nwg, w_first + r, sgs);
-            mlw[r * 4 + 3] = ns > 0 ? (float)((sgs[0].g == g) ? 0 : 1) : -1.f;
+            mlw[r * 8 + 7] = ns > 0 ? (float)((sgs[0].g == g) ? 0 : 1) : -1.f;
           }
           wg_sync();
           // 2. one poll round: every word of every record into LDS
@@ -1129,7 +1134,7 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
               addr[k] = D.REC;
               if (i < nrec * rw) {
                 const int r = i / rw, off = i % rw;
-                const int si = (int)mlw[r * 4 + 3];
+                const int si = (int)mlw[r * 8 + 7];
                 if (si >= 0) {
                   addr[k] = D.REC + (((uint64_t)l * D.nwg + w_first + r) * 2 + si) * rw + off;
                   mask |= 1u << k;
@@ -1179,19 +1184,32 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
           }
           wg_sync();
           if (aborted(D)) { __builtin_amdgcn_s_waitcnt(kWaitAllVm); return; }
-          // 3. combine: o = sum_r exp2(m_r - M) O_r / sum_r exp2(m_r - M) l_r
+          // 3. combine: o = sum_r c_r O_r with c_r = exp2(m_r - M) / L and
+          //    L = sum_r exp2(m_r - M) l_r.  First one wave per query head
+          //    computes every record's weight (lanes over records), then
+          //    every output sums its column with independent LDS reads.
+          if (D.wave < G) {
+            const int h = D.wave;
+            float M = -INFINITY;
+            for (int r = D.lane; r < nrec; r += kWave) M = fmaxf(M, recs[(r * G + h) * (hd + 2)]);
+            M = wave_max(M);
+            float Ls = 0.f;
+            for (int r = D.lane; r < nrec; r += kWave) {
+              const float* rr = recs + (r * G + h) * (hd + 2);
+              Ls += (rr[0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(rr[0] - M)) * rr[1];
+            }
+            Ls = wave_sum(Ls);
+            for (int r = D.lane; r < nrec; r += kWave) {
+              const float* rr = recs + (r * G + h) * (hd + 2);
+              mlw[r * 8 + h] = (rr[0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(rr[0] - M)) / Ls;
+            }
+          }
+          wg_sync();
           for (int t = D.tid; t < G * hd; t += kThreads) {
             const int h = t / hd, dd = t % hd;
-            float M = -INFINITY;
-            for (int r = 0; r < nrec; ++r) M = fmaxf(M, recs[(r * G + h) * (hd + 2)]);
-            float Ls = 0.f, o = 0.f;
-            for (int r = 0; r < nrec; ++r) {
-              const float* rr = recs + (r * G + h) * (hd + 2);
-              const float a = rr[0] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(rr[0] - M);
-              Ls += a * rr[1];
-              o += a * rr[2 + dd];
-            }
-            o = o / Ls;
+            float o = 0.f;
+#pragma unroll 4
+            for (int r = 0; r < nrec; ++r) o += mlw[r * 8 + h] * recs[(r * G + h) * (hd + 2) + 2 + dd];
             ll_storef(D.OB + (uint64_t)l * qd + (uint64_t)(g * G + h) * hd + dd, o, epoch);
           }
         }

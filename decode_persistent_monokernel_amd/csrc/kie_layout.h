@@ -215,33 +215,34 @@ KIE_HD void gemv_wave_chunks(int nrows, int K, int wave, int* c0, int* c1) {
   wave_split(gemv_chunks(nrows, K), wave, c0, c1);
 }
 
-// attention: the n_ctx keys of every KV head are laid end to end
-// (f = g * n_ctx + t) and cut into nwg contiguous ranges; each workgroup range
-// meets at most two heads ("segments"); each segment is cut into kWaves
-// contiguous key ranges, one per wave.
+// attention: the workgroups are cut into Hkv contiguous groups (split), one
+// per KV head, and the n_ctx keys of head g into one contiguous range per
+// workgroup of its group, so no workgroup meets two heads and every one that
+// has keys has exactly one "segment"; each segment is cut into kWaves
+// contiguous key ranges, one per wave (wave_split).  The last workgroup of a
+// group holds the newest key and merges the group's partial results.
 struct AttnSeg {
   int g;       // KV head
   int ta, tb;  // workgroup's keys [ta, tb) of head g
 };
+KIE_HD int attn_head(int Hkv, int nwg, int wg) { return split_owner(wg, nwg, Hkv); }
 KIE_HD int attn_segments(int Hkv, int n_ctx, int nwg, int wg, AttnSeg* seg) {
-  int fa, fb;
-  split(Hkv * n_ctx, nwg, wg, &fa, &fb);
-  int n = 0;
-  while (fa < fb && n < 2) {
-    const int g = fa / n_ctx;
-    const int end = (g + 1) * n_ctx < fb ? (g + 1) * n_ctx : fb;
-    seg[n].g = g;
-    seg[n].ta = fa - g * n_ctx;
-    seg[n].tb = end - g * n_ctx;
-    ++n;
-    fa = end;
-  }
-  return n;
+  const int g = attn_head(Hkv, nwg, wg);
+  int w0, w1, ta, tb;
+  split(nwg, Hkv, g, &w0, &w1);
+  split(n_ctx, w1 - w0, wg - w0, &ta, &tb);
+  if (ta >= tb) return 0;
+  seg[0].g = g;
+  seg[0].ta = ta;
+  seg[0].tb = tb;
+  return 1;
 }
 
 // workgroup that holds key t of head g
 KIE_HD int attn_owner(int Hkv, int n_ctx, int nwg, int g, int t) {
-  return split_owner(g * n_ctx + t, Hkv * n_ctx, nwg);
+  int w0, w1;
+  split(nwg, Hkv, g, &w0, &w1);
+  return w0 + split_owner(t, n_ctx, w1 - w0);
 }
 
 // lanes per key (16 bytes of a key row per lane) and keys per wave load
@@ -307,13 +308,14 @@ KIE_HD LdsPlan lds_plan(const Dims& m, int nwg) {
   const int gemv_sz = kmax + (int)align_up((uint64_t)rmax * kWaves, 64);
   // attention: per-wave records (2 segments x kWaves), later reused by the
   // merger for the records of every workgroup that met its head, then
-  // 4 floats per record, then per segment the G query heads and the key and
-  // value at the current position
+  // 8 floats per record (its weight for each query head, its segment), then
+  // per segment the G query heads and the key and value at the current
+  // position
   const int wrec_sz = imax(2 * kWaves * m.G * (m.hd + 2), max_recs * m.G * (m.hd + 2));
   p.attn_wrec = o;
   p.attn_ml = o + wrec_sz;
-  p.attn_qkv = p.attn_ml + max_recs * 4;
-  const int attn_sz = wrec_sz + max_recs * 4 + 2 * (m.G + 2) * m.hd;
+  p.attn_qkv = p.attn_ml + max_recs * 8;
+  const int attn_sz = wrec_sz + max_recs * 8 + 2 * (m.G + 2) * m.hd;
   o += (int)align_up((uint64_t)imax(gemv_sz, attn_sz), 64);
   p.own = o; o += (int)align_up((uint64_t)2 * ((m.d + nwg - 1) / nwg), 64);
   p.desc = o; o += kDescInts;
