@@ -60,6 +60,7 @@ std::string check_config(const kie_model_config& c) {
   if (c.head_dim % 8) return "head_dim must be a multiple of 8";
   if (c.d_model % 8 || (c.n_heads * c.head_dim) % 8 || c.ffn_dim % 8)
     return "d_model, n_heads*head_dim and ffn_dim must be multiples of 8";
+  if (c.vocab % 2) return "vocab must be even (the LM head is stored as row pairs)";
   if (c.n_lanes <= 0 || c.n_heads % c.n_lanes || c.ffn_dim % c.n_lanes)
     return "n_lanes must divide n_heads and ffn_dim";
   if (c.parallel_block != 0 && c.parallel_block != 1) return "parallel_block must be 0 or 1";
@@ -106,11 +107,19 @@ std::string check_supported(const kie::Dims& m, int nwg) {
 // ---------------------------------------------------------------------------
 void copy_rows(uint16_t* dst, const uint16_t* src, size_t n) { std::memcpy(dst, src, n * sizeof(uint16_t)); }
 
-// n rows of k elements from src (stride k) to dst (stride row_stride(k))
-void copy_matrix(uint16_t* dst, const uint16_t* src, size_t n, int k) {
-  const size_t rs = kie::row_stride(k);
-  if (rs == (size_t)k) return copy_rows(dst, src, n * k);
-  for (size_t r = 0; r < n; ++r) copy_rows(dst + r * rs, src + r * k, k);
+// n rows of k columns into the row-pair chunk layout (kie_layout.h), packed
+// row r read from src_row(r); dst is zeroed beforehand, so the columns past
+// k stay zero
+template <class RowFn>
+void pack_matrix(uint16_t* dst, size_t n, int k, RowFn src_row) {
+  const int nb = kie::col_blocks(k);
+  for (size_t r = 0; r < n; ++r) {
+    const uint16_t* s = src_row(r);
+    for (int b = 0; b < nb; ++b) {
+      const int c0 = b * kie::kPairCols;
+      copy_rows(dst + kie::packed_at(r, c0, k), s + c0, (size_t)std::min(kie::kPairCols, k - c0));
+    }
+  }
 }
 
 bool weights_complete(const kie_model_config& c, const kie_weights* w) {
@@ -127,23 +136,20 @@ bool weights_complete(const kie_model_config& c, const kie_weights* w) {
 // pack layer l into dst (layer_stride elements)
 void pack_layer(const kie::Dims& m, const kie::PackLayout& pl, const kie_weights* w, int l, uint16_t* dst) {
   const size_t d = m.d, qd = (size_t)m.H * m.hd, F = m.F;
-  const size_t sd = kie::row_stride(m.d);
   std::memset(dst, 0, pl.layer_stride * sizeof(uint16_t));
   copy_rows(dst + pl.attn_norm, w->attn_norm[l], d);
-  const int rows = (m.H + 2 * m.Hkv) * m.hd;
-  for (int r = 0; r < rows; ++r) {
+  const size_t rows = (size_t)(m.H + 2 * m.Hkv) * m.hd;
+  pack_matrix(dst + pl.wqkv, rows, m.d, [&](size_t r) {
     int which, src;
-    kie::qkv_source_row(m, r, &which, &src);
+    kie::qkv_source_row(m, (int)r, &which, &src);
     const uint16_t* s = which == 0 ? w->wq[l] : which == 1 ? w->wk[l] : w->wv[l];
-    copy_rows(dst + pl.wqkv + (size_t)r * sd, s + (size_t)src * d, d);
-  }
-  copy_matrix(dst + pl.wo, w->wo[l], d, (int)qd);
+    return s + (size_t)src * d;
+  });
+  pack_matrix(dst + pl.wo, d, (int)qd, [&](size_t r) { return w->wo[l] + r * qd; });
   copy_rows(dst + pl.mlp_norm, w->mlp_norm[l], d);
-  for (size_t f = 0; f < F; ++f) {
-    copy_rows(dst + pl.wgu + (2 * f) * sd, w->w_gate[l] + f * d, d);
-    copy_rows(dst + pl.wgu + (2 * f + 1) * sd, w->w_up[l] + f * d, d);
-  }
-  copy_matrix(dst + pl.wd, w->w_down[l], d, (int)F);
+  pack_matrix(dst + pl.wgu, 2 * F, m.d,
+              [&](size_t r) { return (r & 1 ? w->w_up[l] : w->w_gate[l]) + (r >> 1) * d; });
+  pack_matrix(dst + pl.wd, d, (int)F, [&](size_t r) { return w->w_down[l] + r * F; });
 }
 
 // the part after the layers: final_norm, lm_head, embed
@@ -151,7 +157,8 @@ void pack_tail(const kie::Dims& m, const kie::PackLayout& pl, const kie_weights*
   const uint64_t base = pl.final_norm;
   std::memset(dst_at_final_norm, 0, (pl.total - base) * sizeof(uint16_t));
   copy_rows(dst_at_final_norm + (pl.final_norm - base), w->final_norm, m.d);
-  copy_matrix(dst_at_final_norm + (pl.lm_head - base), w->lm_head, (size_t)m.V, m.d);
+  pack_matrix(dst_at_final_norm + (pl.lm_head - base), (size_t)m.V, m.d,
+              [&](size_t r) { return w->lm_head + r * (size_t)m.d; });
   copy_rows(dst_at_final_norm + (pl.embed - base), w->embed, (size_t)m.V * m.d);
 }
 
@@ -479,13 +486,13 @@ kie_status kie_validate_schedule(const kie_model_config* cfg, int32_t nwg, int32
         owner[r] = w;
       }
       // chunks of the workgroup's packed stretch: contiguous per wave, every
-      // packed element of its rows read by exactly one wave
-      const int rs = kie::row_stride(sh.K);
+      // packed element of its row pairs read by exactly one wave
       const int nch = kie::gemv_chunks(r1 - r0, sh.K);
-      const int64_t elems = (int64_t)(r1 - r0) * rs;
-      if ((int64_t)nch * kie::kBlock < elems || (nch > 0 && (int64_t)(nch - 1) * kie::kBlock >= elems))
+      if ((uint64_t)nch * kie::kBlock != kie::packed_elems((uint64_t)(r1 - r0), sh.K))
         return bad("chunk count does not match the workgroup rows");
-      if (rs < kie::kBlock) return bad("row stride below one chunk");
+      if (kie::packed_at((uint64_t)r0, 0, sh.K) + (uint64_t)nch * kie::kBlock !=
+          kie::packed_at((uint64_t)r1, 0, sh.K))
+        return bad("workgroup chunks are not contiguous");
       int prev_end = 0;
       for (int wave = 0; wave < kie::kWaves; ++wave) {
         int c0, c1;

@@ -372,15 +372,14 @@ KIE_DI void write_gemv_desc(const KParams& p, int kind, int nwg, int wg, int wav
   int r0, r1, c0, c1;
   gemv_rows(p.m, kind, nwg, wg, &r0, &r1);
   gemv_wave_chunks(r1 - r0, sh.K, wave, &c0, &c1);
-  const int rs = row_stride(sh.K);
-  const int e0 = c0 * kBlock;
-  const uint64_t off = matrix_offset(p, kind) + (uint64_t)r0 * (uint64_t)rs + (uint64_t)e0;
+  const int nb = col_blocks(sh.K);
+  const uint64_t off = matrix_offset(p, kind) + packed_at((uint64_t)r0, 0, sh.K) + (uint64_t)c0 * kBlock;
   dsc[0] = (int)(uint32_t)off;
   dsc[1] = (int)(uint32_t)(off >> 32);
   dsc[2] = c1 - c0;
-  dsc[3] = e0 / rs;
-  dsc[4] = e0 % rs;
-  dsc[5] = rs;
+  dsc[3] = c0 / nb;  // first row pair (from the workgroup's first row)
+  dsc[4] = c0 % nb;  // first column block
+  dsc[5] = nb;
   dsc[6] = 0;
   dsc[7] = 0;
   if (wave == 0) {
@@ -625,94 +624,89 @@ KIE_DI void unpack8(const u4v x, float* v) {
 }
 
 // ---------------------------------------------------------------------------
-// GEMV stream: consume this wave's nch chunks of the workgroup's packed rows
-// (row stride rs; the first chunk starts at column S of row R) and write one
-// partial sum per (row, wave) into part.  A chunk meets at most two rows: the
-// lanes still in row R finish it, the others start row R + 1.
+// GEMV stream: consume this wave's nch chunks of the workgroup's row pairs
+// (the first is column block b of pair P; nb blocks per pair) and write one
+// partial sum per (row, wave) into part.  Lanes 0..31 accumulate row 2P and
+// lanes 32..63 row 2P+1 over the pair's blocks; the cross-lane sums happen
+// when the pair (or the wave's share of it) ends.
 // ---------------------------------------------------------------------------
-// one chunk's dot product, chained onto `init`
-KIE_DI float dot_chunk(const u4v w, const f4v a, const f4v b, float init) {
-  float t = init;
-  t = __builtin_fmaf(h2f_lo(w.x), a.x, t);
-  t = __builtin_fmaf(h2f_hi(w.x), a.y, t);
-  t = __builtin_fmaf(h2f_lo(w.y), a.z, t);
-  t = __builtin_fmaf(h2f_hi(w.y), a.w, t);
-  t = __builtin_fmaf(h2f_lo(w.z), b.x, t);
-  t = __builtin_fmaf(h2f_hi(w.z), b.y, t);
-  t = __builtin_fmaf(h2f_lo(w.w), b.z, t);
-  t = __builtin_fmaf(h2f_hi(w.w), b.w, t);
-  return t;
+// one chunk's 8 products for this lane, summed as two independent chains
+KIE_DI float dot_chunk(const u4v w, const f4v a, const f4v b) {
+  float t0 = h2f_lo(w.x) * a.x;
+  float t1 = h2f_lo(w.z) * b.x;
+  t0 = __builtin_fmaf(h2f_hi(w.x), a.y, t0);
+  t1 = __builtin_fmaf(h2f_hi(w.z), b.y, t1);
+  t0 = __builtin_fmaf(h2f_lo(w.y), a.z, t0);
+  t1 = __builtin_fmaf(h2f_lo(w.w), b.z, t1);
+  t0 = __builtin_fmaf(h2f_hi(w.y), a.w, t0);
+  t1 = __builtin_fmaf(h2f_hi(w.w), b.w, t1);
+  return t0 + t1;
 }
 
 struct GemvAcc {
   float* part;
-  float A;
-  int R, S, rs, wave, lane8, lane;
-  // fold one chunk (row R from column S) into the accumulator
-  KIE_DI void chunk(const u4v w, const f4v a, const f4v b) {
-    const bool inR = S + lane8 < rs;
-    const float t = dot_chunk(w, a, b, inR ? A : 0.f);
-    if (S + kBlock < rs) {
-      A = t;
-      S += kBlock;
-    } else {
-      // Row R ends in this chunk.  A lane still in row R finishes it with t;
-      // a lane past the end starts row R + 1 with t, and its earlier chunks
-      // of row R are in A.
-      const float sum = wave_sum(inR ? t : A);
-      if (lane == 0) part[R * kWaves + wave] = sum;
-      A = inR ? 0.f : t;
-      ++R;
-      S += kBlock - rs;
-    }
+  float A;  // this lane's sum for its row of pair P over the blocks so far
+  int P, b, nb, wave, lane;
+  // the pair's two row sums: a 16-lane sum in every row of the wave, then
+  // row 1 adds row 0 and row 3 adds row 2 (row_bcast:15); lane 31 holds row
+  // 2P, lane 63 row 2P+1
+  KIE_DI void flush() {
+    const float r = row16_sum(A);
+    const float s = r + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(r), 0x142, 0xA, 0xF, false));
+    if ((lane & 31) == 31) part[(2 * P + (lane >> 5)) * kWaves + wave] = s;
+    A = 0.f;
+    b = 0;
+    ++P;
+  }
+  KIE_DI void fold(float t) {
+    A += t;
+    if (++b == nb) flush();
   }
 };
 
-KIE_DI void gemv_stream(const Dev& D, Cursor& cur, int& slot, const float* xs, float* part, int nch, int R, int S,
-                        int rs, int nrows) {
+KIE_DI void gemv_stream(const Dev& D, Cursor& cur, int& slot, const float* xs, float* part, int nch, int P, int b,
+                        int nb) {
   make_uniform(cur, slot);
-  const uint32_t xs0 = (uint32_t)(uintptr_t)xs;
+  // this lane's input columns 8 * (lane % 32) .. +8 of block 0: a float4 in
+  // each plane (lanes l and l + 32 read the same words)
+  const uint32_t xl = (uint32_t)(uintptr_t)xs + (uint32_t)(D.lane & 31) * 16u;
   const uint32_t pb = (uint32_t)D.plane * 4u;
-  GemvAcc g{part, 0.f, R, S, rs, D.wave, D.lane * 8, D.lane};
+  GemvAcc g{part, 0.f, P, b, nb, D.wave, D.lane};
   int j = 0;
-  if (rs >= 4 * kBlock) {
-    // four chunks per LDS round trip; they meet at most two rows
-    for (; j + 4 <= nch; j += 4) {
-      uint32_t ra[4], xa[8];
+  // four chunks per LDS round trip
+  for (; j + 4 <= nch; j += 4) {
+    uint32_t ra[4], xa[8];
+    int bb = g.b;
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int er = g.S + k * kBlock + g.lane8;
-        const int col = er < rs ? er : er - rs;
-        xa[2 * k] = xs0 + (uint32_t)col * 2u;
-        xa[2 * k + 1] = xa[2 * k] + pb;
-        ra[k] = ring_addr(D, ring_add(slot, k));
-      }
-      __builtin_amdgcn_s_waitcnt(kWaitRing4);
-      u4v w[4];
-      f4v a[4], b[4];
-      read_w_x4(ra, xa, w, a, b);
-      cursor_issue4(D, cur, slot);
-      slot = ring_add(slot, 4);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) g.chunk(w[k], a[k], b[k]);
+    for (int k = 0; k < 4; ++k) {
+      xa[2 * k] = xl + (uint32_t)bb * 512u;
+      xa[2 * k + 1] = xa[2 * k] + pb;
+      bb = bb + 1 == nb ? 0 : bb + 1;
+      ra[k] = ring_addr(D, ring_add(slot, k));
     }
+    __builtin_amdgcn_s_waitcnt(kWaitRing4);
+    u4v w[4];
+    f4v a[4], c[4];
+    read_w_x4(ra, xa, w, a, c);
+    cursor_issue4(D, cur, slot);
+    slot = ring_add(slot, 4);
+    float t[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) t[k] = dot_chunk(w[k], a[k], c[k]);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) g.fold(t[k]);
   }
   for (; j < nch; ++j) {
-    const int er = g.S + g.lane8;
-    const int col = er < rs ? er : er - rs;
-    const uint32_t xa = xs0 + (uint32_t)col * 2u;  // float4 number col/8 of plane 0
+    const uint32_t xa = xl + (uint32_t)g.b * 512u;
     __builtin_amdgcn_s_waitcnt(kWaitRing);
     u4v w;
-    f4v a, b;
-    read_w_x(ring_addr(D, slot), xa, xa + pb, w, a, b);
+    f4v a, c;
+    read_w_x(ring_addr(D, slot), xa, xa + pb, w, a, c);
     cursor_issue(D, cur, slot);
     slot = ring_next(slot);
-    g.chunk(w, a, b);
+    g.fold(dot_chunk(w, a, c));
   }
-  if (g.S > 0 && g.R < nrows) {
-    const float sum = wave_sum(g.A);
-    if (D.lane == 0) part[g.R * kWaves + D.wave] = sum;
-  }
+  if (g.b > 0) g.flush();
 }
 
 // ---------------------------------------------------------------------------
@@ -801,7 +795,7 @@ KIE_DI void rmsnorm_to_xs(const Dev& D, const float* xraw, const uint16_t (&gr)[
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) tot += D.sh->redf[w];
   const float inv = 1.0f / sqrtf(tot / (float)d + p.m.eps);
-  const int padded = row_stride(d);
+  const int padded = padded_cols(d);
 #pragma unroll
   for (int k = 0; k < kGainRegs; ++k) {
     const int i = D.tid + k * kThreads;
@@ -809,9 +803,9 @@ KIE_DI void rmsnorm_to_xs(const Dev& D, const float* xraw, const uint16_t (&gr)[
   }
 }
 
-// the zero columns of a padded row (row_stride(K) > K)
+// the zero columns of a padded row (padded_cols(K) > K)
 KIE_DI void zero_tail(const Dev& D, float* xs, int K) {
-  const int padded = row_stride(K);
+  const int padded = padded_cols(K);
   for (int i = K + D.tid; i < padded; i += kThreads) xs[xs_pos(i, D.plane)] = 0.f;
 }
 
@@ -1271,7 +1265,7 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
 
       {
         const int* gd = D.desc + D.wave * kWaveDesc + 8 * gi;
-        gemv_stream(D, cur, slot, xs, part, rfl(gd[2]), rfl(gd[3]), rfl(gd[4]), rfl(gd[5]), nrows);
+        gemv_stream(D, cur, slot, xs, part, rfl(gd[2]), rfl(gd[3]), rfl(gd[4]), rfl(gd[5]));
       }
       stamp(D, s, ph, 2);
       wg_sync();

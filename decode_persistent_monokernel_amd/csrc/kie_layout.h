@@ -22,6 +22,7 @@ constexpr int kThreads = kWave * kWaves;
 constexpr int kBlock = 512;             // fp16 elements one wave reads with 16 B per lane (a chunk)
 constexpr int kBlock8 = kBlock / 8;     // 16-byte segments per chunk (= lanes)
 constexpr int kChunkBytes = kBlock * 2;
+constexpr int kPairCols = kBlock / 2;   // columns of each of the two rows in a GEMV chunk
 constexpr int kGainRegs = 8;            // RMSNorm gains per thread: d <= kGainRegs * kThreads
 
 enum PhaseKind : int { PH_QKV = 0, PH_ATTN = 1, PH_O = 2, PH_GU = 3, PH_DOWN = 4, PH_LM = 5 };
@@ -45,10 +46,14 @@ struct Dims {
 //
 // Per layer, in order: attn_norm[d], Wqkv[(H+2Hkv)hd][d], Wo[d][H hd],
 // mlp_norm[d], Wgu[2F][d], Wd[d][F]; then final_norm[d], Wlm[V][d], E[V][d].
-// Matrices stay row-major [out][in] (a row is the contiguous K-vector one
-// output consumes), rows kept apart by row_stride(K) elements (K itself, or
-// 512 with a zero tail when K < 512, so that a 1-KB chunk never spans more
-// than two rows), with two row permutations:
+// A matrix with R rows (R even) and K columns is stored as R/2 row pairs,
+// each cut into col_blocks(K) blocks of 256 columns; block b of pair p is
+// one 1-KB chunk at ((p * col_blocks(K) + b) * 512): 256 columns of row 2p,
+// then the same 256 columns of row 2p+1 (columns past K are zero).  A wave
+// reading the chunk with 16 bytes per lane gives lanes 0..31 eight columns
+// of row 2p each and lanes 32..63 the same columns of row 2p+1, so a lane
+// keeps one row's partial sum for all its chunks of the pair and the cross-
+// lane sum happens once per pair.  Packed rows are permuted twice:
 //   * Wqkv: inside every q and k head, packed row 2i is dim i and row 2i+1 is
 //     dim i + hd/2, so the rotate-half RoPE pair of an output sits in one
 //     workgroup; v rows are in natural order;
@@ -58,7 +63,14 @@ struct Dims {
 // the buffer.  The embedding table keeps stride d (it is gathered, not
 // streamed).
 // ---------------------------------------------------------------------------
-KIE_HD int row_stride(int K) { return K < kBlock ? kBlock : K; }
+KIE_HD int col_blocks(int K) { return (K + kPairCols - 1) / kPairCols; }
+KIE_HD int padded_cols(int K) { return col_blocks(K) * kPairCols; }
+KIE_HD uint64_t packed_elems(uint64_t rows, int K) { return rows / 2 * (uint64_t)col_blocks(K) * kBlock; }
+// packed offset of element (r, c) of a matrix with K columns
+KIE_HD uint64_t packed_at(uint64_t r, int c, int K) {
+  return ((r >> 1) * (uint64_t)col_blocks(K) + (uint64_t)(c / kPairCols)) * kBlock + (r & 1) * kPairCols +
+         (uint64_t)(c % kPairCols);
+}
 
 struct PackLayout {
   uint64_t layer_stride;
@@ -74,17 +86,16 @@ KIE_HD PackLayout pack_layout(const Dims& m) {
   PackLayout p{};
   uint64_t o = 0;
   const uint64_t d = m.d, qd = (uint64_t)m.H * m.hd, kvd = (uint64_t)m.Hkv * m.hd, F = m.F;
-  const uint64_t sd = row_stride(m.d), sq = row_stride(m.H * m.hd), sf = row_stride(m.F);
   p.attn_norm = o; o = align_up(o + d, A);
-  p.wqkv = o; o = align_up(o + (qd + 2 * kvd) * sd, A);
-  p.wo = o; o = align_up(o + d * sq, A);
+  p.wqkv = o; o = align_up(o + packed_elems(qd + 2 * kvd, m.d), A);
+  p.wo = o; o = align_up(o + packed_elems(d, m.H * m.hd), A);
   p.mlp_norm = o; o = align_up(o + d, A);
-  p.wgu = o; o = align_up(o + 2 * F * sd, A);
-  p.wd = o; o = align_up(o + d * sf, A);
+  p.wgu = o; o = align_up(o + packed_elems(2 * F, m.d), A);
+  p.wd = o; o = align_up(o + packed_elems(d, m.F), A);
   p.layer_stride = o;
   o = p.layer_stride * (uint64_t)m.L;
   p.final_norm = o; o = align_up(o + d, A);
-  p.lm_head = o; o = align_up(o + (uint64_t)m.V * sd, A);
+  p.lm_head = o; o = align_up(o + packed_elems(m.V, m.d), A);
   p.embed = o; o = align_up(o + (uint64_t)m.V * d, A);
   p.total = o + kBlock;
   return p;
@@ -182,17 +193,18 @@ KIE_HD int split_owner(int f, int n, int parts) {
   return (int)(((uint32_t)(f + 1) * (uint32_t)parts + (uint32_t)n - 1) / (uint32_t)n) - 1;
 }
 
-// GEMV ops: rows, columns and row grouping of each phase
+// GEMV ops: rows, columns and row grouping of each phase (a workgroup owns
+// whole row pairs: the packed chunks hold two rows)
 struct GemvShape {
   int rows, K, unit_rows;  // unit_rows rows always stay in one workgroup
 };
 KIE_HD GemvShape gemv_shape(const Dims& m, int kind) {
   switch (kind) {
     case PH_QKV: return {(m.H + 2 * m.Hkv) * m.hd, m.d, 2};
-    case PH_O: return {m.d, m.H * m.hd, 1};
+    case PH_O: return {m.d, m.H * m.hd, 2};
     case PH_GU: return {2 * m.F, m.d, 2};
-    case PH_DOWN: return {m.d, m.F, 1};
-    default: return {m.V, m.d, 1};  // PH_LM
+    case PH_DOWN: return {m.d, m.F, 2};
+    default: return {m.V, m.d, 2};  // PH_LM
   }
 }
 KIE_HD int blocks_per_row(int K) { return (K + kBlock - 1) / kBlock; }
@@ -207,10 +219,9 @@ KIE_HD void gemv_rows(const Dims& m, int kind, int nwg, int wg, int* r0, int* r1
   *r1 = b * s.unit_rows;
 }
 
-// The workgroup's rows are one contiguous stretch of nrows * row_stride(K)
-// packed elements, read as 1-KB chunks (the last one may run past the end);
-// wave w takes chunks [c0, c1).  A chunk meets at most two rows.
-KIE_HD int gemv_chunks(int nrows, int K) { return ceil_div(nrows * row_stride(K), kBlock); }
+// The workgroup's row pairs are one contiguous stretch of nrows / 2 *
+// col_blocks(K) chunks; wave w takes chunks [c0, c1).
+KIE_HD int gemv_chunks(int nrows, int K) { return nrows / 2 * col_blocks(K); }
 KIE_HD void gemv_wave_chunks(int nrows, int K, int wave, int* c0, int* c1) {
   wave_split(gemv_chunks(nrows, K), wave, c0, c1);
 }
@@ -285,8 +296,8 @@ KIE_HD int imax(int a, int b) { return a > b ? a : b; }
 KIE_HD LdsPlan lds_plan(const Dims& m, int nwg) {
   LdsPlan p{};
   // GEMV input: two planes of kmax/2 floats (elements 8g..8g+3 at plane 0,
-  // 8g+4..8g+7 at plane 1, position 4g), covering row_stride(K) elements
-  int kmax = imax(imax(imax(row_stride(m.d), row_stride(m.H * m.hd)), row_stride(m.F)), 2 * nwg);
+  // 8g+4..8g+7 at plane 1, position 4g), covering padded_cols(K) elements
+  int kmax = imax(imax(imax(padded_cols(m.d), padded_cols(m.H * m.hd)), padded_cols(m.F)), 2 * nwg);
   kmax = (int)align_up((uint64_t)kmax, kBlock);
   int rmax = 0;
   for (int k = 0; k <= PH_LM; ++k) {

@@ -88,13 +88,25 @@ def test_host_only_context_refuses_gpu_calls():
         L.kie_destroy(ctx)
 
 
-def _rs(k):
-    """row stride of a packed matrix with k columns: k, or 512 when k < 512"""
-    return max(k, 512)
+def _nb(k):
+    """256-column blocks of a packed row"""
+    return (k + 255) // 256
+
+
+def _psize(rows, k):
+    """packed elements of a rows x k matrix: one 512-element chunk per (row pair, block)"""
+    return rows // 2 * _nb(k) * 512
+
+
+def _full(flat, rows, k):
+    """undo the row-pair chunk layout: chunk (p, b) = 256 columns of row 2p, then
+    the same columns of row 2p+1; returns rows x (256 * blocks) with the pads"""
+    c = flat[: _psize(rows, k)].reshape(rows // 2, _nb(k), 2, 256)
+    return c.transpose(0, 2, 1, 3).reshape(rows, _nb(k) * 256)
 
 
 def _mat(flat, rows, k):
-    return flat[: rows * _rs(k)].reshape(rows, _rs(k))[:, :k]
+    return _full(flat, rows, k)[:, :k]
 
 
 def _unpack(cfg: ModelConfig, packed: np.ndarray, offsets):
@@ -106,7 +118,7 @@ def _unpack(cfg: ModelConfig, packed: np.ndarray, offsets):
         base = l * stride
         g = lambda off, n: packed[base + off: base + off + n]
         out[f"layers.{l}.attn_norm"] = g(offsets["attn_norm"], d)
-        qkv = _mat(g(offsets["wqkv"], (H + 2 * Hkv) * hd * _rs(d)), (H + 2 * Hkv) * hd, d)
+        qkv = _mat(g(offsets["wqkv"], _psize((H + 2 * Hkv) * hd, d)), (H + 2 * Hkv) * hd, d)
         def unperm(block, heads):
             blk = block.reshape(heads, hd, d)
             o = np.empty_like(blk)
@@ -116,12 +128,12 @@ def _unpack(cfg: ModelConfig, packed: np.ndarray, offsets):
         out[f"layers.{l}.wq"] = unperm(qkv[: H * hd], H)
         out[f"layers.{l}.wk"] = unperm(qkv[H * hd: (H + Hkv) * hd], Hkv)
         out[f"layers.{l}.wv"] = qkv[(H + Hkv) * hd:]
-        out[f"layers.{l}.wo"] = _mat(g(offsets["wo"], d * _rs(H * hd)), d, H * hd)
+        out[f"layers.{l}.wo"] = _mat(g(offsets["wo"], _psize(d, H * hd)), d, H * hd)
         out[f"layers.{l}.mlp_norm"] = g(offsets["mlp_norm"], d)
-        gu = _mat(g(offsets["wgu"], 2 * F * _rs(d)), 2 * F, d)
+        gu = _mat(g(offsets["wgu"], _psize(2 * F, d)), 2 * F, d)
         out[f"layers.{l}.w_gate"] = gu[0::2]
         out[f"layers.{l}.w_up"] = gu[1::2]
-        out[f"layers.{l}.w_down"] = _mat(g(offsets["wd"], d * _rs(F)), d, F)
+        out[f"layers.{l}.w_down"] = _mat(g(offsets["wd"], _psize(d, F)), d, F)
     out["final_norm"] = packed[offsets["final_norm"]: offsets["final_norm"] + d]
     out["lm_head"] = _mat(packed[offsets["lm_head"]:], cfg.vocab, d)
     out["embed"] = packed[offsets["embed"]: offsets["embed"] + cfg.vocab * d].reshape(cfg.vocab, d)
@@ -135,15 +147,15 @@ def _offsets(cfg):
     o = {}
     x = 0
     o["attn_norm"] = x; x = a(x + d)
-    o["wqkv"] = x; x = a(x + (qd + 2 * kvd) * _rs(d))
-    o["wo"] = x; x = a(x + d * _rs(qd))
+    o["wqkv"] = x; x = a(x + _psize(qd + 2 * kvd, d))
+    o["wo"] = x; x = a(x + _psize(d, qd))
     o["mlp_norm"] = x; x = a(x + d)
-    o["wgu"] = x; x = a(x + 2 * F * _rs(d))
-    o["wd"] = x; x = a(x + d * _rs(F))
+    o["wgu"] = x; x = a(x + _psize(2 * F, d))
+    o["wd"] = x; x = a(x + _psize(d, F))
     o["layer_stride"] = x
     x = x * cfg.n_layers
     o["final_norm"] = x; x = a(x + d)
-    o["lm_head"] = x; x = a(x + cfg.vocab * _rs(d))
+    o["lm_head"] = x; x = a(x + _psize(cfg.vocab, d))
     o["embed"] = x
     return o
 
@@ -166,12 +178,13 @@ def test_packer_is_a_permutation(cfg):
     back = _unpack(cfg, packed, off)
     for k, v in w.items():
         assert np.array_equal(back[k], v.view(np.uint16)), k
-    # the kernel streams whole 1-KB chunks: row pads and the tail slack are zeros
+    # the kernel streams whole 1-KB chunks: column pads and the tail slack are zeros
     assert not packed[-512:].any()
-    d, rows = cfg.d_model, (cfg.n_heads + 2 * cfg.n_kv_heads) * cfg.head_dim
-    if _rs(d) > d:
-        qkv = packed[off["wqkv"]: off["wqkv"] + rows * _rs(d)].reshape(rows, _rs(d))
-        assert not qkv[:, d:].any()
+    d, qd, F = cfg.d_model, cfg.q_dim, cfg.ffn_dim
+    rows = (cfg.n_heads + 2 * cfg.n_kv_heads) * cfg.head_dim
+    for name, r, k in (("wqkv", rows, d), ("wo", d, qd), ("wgu", 2 * F, d), ("wd", d, F)):
+        full = _full(packed[off[name]:], r, k)
+        assert not full[:, k:].any(), name
 
 
 @needs_lib
