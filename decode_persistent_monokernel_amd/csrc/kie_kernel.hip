@@ -82,6 +82,19 @@ KIE_DI float wave_max(float v) {
   return v;
 }
 // sum over groups of `lpk` consecutive lanes; every lane of a group gets it
+// greedy order: the larger value wins, equal values go to the smaller index
+KIE_DI bool argmax_better(float ov, int oi, float bv, int bi) { return ov > bv || (ov == bv && oi < bi); }
+KIE_DI void wave_argmax(float& v, int& i) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float ov = __shfl_xor(v, off);
+    const int oi = __shfl_xor(i, off);
+    if (argmax_better(ov, oi, v, i)) {
+      v = ov;
+      i = oi;
+    }
+  }
+}
 KIE_DI float group_sum(float v, int lpk) {
   if (lpk == 16) return row16_sum(v);
   if (lpk == 8) {
@@ -168,12 +181,14 @@ KIE_DI void online_update(float& m, float& l, float* acc, float s, const float* 
 // ---------------------------------------------------------------------------
 struct Shared {  // small LDS block after the planned area
   int abort;
-  int token;
-  int pad[2];
+  int pad[3];
   float redf[kWaves];
   float lmv[kWaves];
   int lmi[kWaves];
+  float tokv[kWaves];  // end of step: each wave's best (value, index) over the workgroup partials
+  int toki[kWaves];
 };
+static_assert(sizeof(Shared) <= kSharedReserve, "Shared block");
 
 struct Dev {
   const KParams* p;
@@ -191,13 +206,21 @@ struct Dev {
   int lpk, kpl, kl, dl, lane_active;
 };
 
-// the workgroup's abort flag, read after a barrier (uniform)
-KIE_DI bool aborted(const Dev& D) { return rfl(*(volatile int*)&D.sh->abort) != 0; }
+// The workgroup's abort flag.  It is read and written through an LDS-typed
+// pointer: through a generic pointer a volatile access becomes a flat load,
+// which also counts as a vector memory access, and its wait then waits for
+// every ring load in flight.
+typedef __attribute__((address_space(3))) volatile int lds_vint;
+KIE_DI lds_vint* abort_flag(const Dev& D) { return (lds_vint*)(__attribute__((address_space(3))) int*)&D.sh->abort; }
+KIE_DI bool abort_seen(const Dev& D) { return *abort_flag(D) != 0; }
+KIE_DI void set_abort(const Dev& D) { *abort_flag(D) = 1; }
+// the abort flag read after a barrier (uniform)
+KIE_DI bool aborted(const Dev& D) { return rfl(*abort_flag(D)) != 0; }
 
 KIE_DI void raise_status(const Dev& D, int code) {
   atomicCAS(&D.state[0], 0, code);
   __hip_atomic_store(&D.state[1], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  D.sh->abort = 1;
+  set_abort(D);
 }
 
 // spin on one word until its epoch matches; false on timeout / abort
@@ -211,9 +234,9 @@ KIE_DI bool spin_word(const Dev& D, const u64* a, uint32_t epoch, u64* out) {
       return true;
     }
     if ((it & 15) == 15) {
-      if (*(volatile int*)&D.sh->abort) return false;
+      if (abort_seen(D)) return false;
       if (__hip_atomic_load(&D.state[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
-        D.sh->abort = 1;
+        set_abort(D);
         return false;
       }
       if (wall_clock64() - t0 > D.p->timeout_ticks) {
@@ -284,9 +307,9 @@ KIE_DI bool poll_words(const Dev& D, const u64* base, int stride, uint32_t mask,
     if (!stale) return true;
     if (it == 0) t0 = wall_clock64();
     if ((it & 15) == 15) {
-      if (*(volatile int*)&D.sh->abort) return false;
+      if (abort_seen(D)) return false;
       if (__hip_atomic_load(&D.state[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
-        D.sh->abort = 1;
+        set_abort(D);
         return false;
       }
       if (wall_clock64() - t0 > D.p->timeout_ticks) {
@@ -317,9 +340,9 @@ KIE_DI bool poll_addrs(const Dev& D, const u64* const (&a)[N], uint32_t mask, ui
     if (!stale) return true;
     if (it == 0) t0 = wall_clock64();
     if ((it & 15) == 15) {
-      if (*(volatile int*)&D.sh->abort) return false;
+      if (abort_seen(D)) return false;
       if (__hip_atomic_load(&D.state[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
-        D.sh->abort = 1;
+        set_abort(D);
         return false;
       }
       if (wall_clock64() - t0 > D.p->timeout_ticks) {
@@ -783,11 +806,22 @@ KIE_DI void load_gains(const Dev& D, const uint16_t* g, uint16_t (&gr)[kGainRegs
 
 // xraw -> xs = g * x / sqrt(mean(x^2) + eps) in the two-plane layout, zero
 // up to the padded row length
+// This thread's elements are read from LDS once, all together (a loop that
+// re-read xraw between writes to xs would wait out one LDS round trip per
+// element: the compiler cannot tell the two arrays apart).
 KIE_DI void rmsnorm_to_xs(const Dev& D, const float* xraw, const uint16_t (&gr)[kGainRegs], float* xs) {
   const KParams& p = *D.p;
   const int d = p.m.d;
+  const int t = opaque(D.tid);
+  float xv[kGainRegs];
+#pragma unroll
+  for (int k = 0; k < kGainRegs; ++k) {
+    const int i = t + k * kThreads;
+    xv[k] = xraw[i < d ? i : 0];
+  }
   float ss = 0.f;
-  for (int i = D.tid; i < d; i += kThreads) ss += xraw[i] * xraw[i];
+#pragma unroll
+  for (int k = 0; k < kGainRegs; ++k) ss += t + k * kThreads < d ? xv[k] * xv[k] : 0.f;
   ss = wave_sum(ss);
   if (D.lane == 0) D.sh->redf[D.wave] = ss;
   wg_sync();
@@ -798,8 +832,8 @@ KIE_DI void rmsnorm_to_xs(const Dev& D, const float* xraw, const uint16_t (&gr)[
   const int padded = padded_cols(d);
 #pragma unroll
   for (int k = 0; k < kGainRegs; ++k) {
-    const int i = D.tid + k * kThreads;
-    if (i < padded) xs[xs_pos(i, D.plane)] = i < d ? xraw[i] * inv * hbits2f(gr[k]) : 0.f;
+    const int i = t + k * kThreads;
+    if (i < padded) xs[xs_pos(i, D.plane)] = i < d ? xv[k] * inv * hbits2f(gr[k]) : 0.f;
   }
 }
 
@@ -862,7 +896,7 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
   float* own = lds_dyn + p.lp.own;  // parallel block: a_l rows, then own residual rows
   int* wgrows = D.desc + kWaves * kWaveDesc;
 
-  if (D.tid == 0) D.sh->abort = 0;
+  if (D.tid == 0) *abort_flag(D) = 0;
   // descriptors: every lane of a wave computes, lane 0 stores
   {
     int dsc[8], rows[2];
@@ -1146,9 +1180,9 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
                 if ((mask & (1u << k)) && ll_epoch(vv[k]) != epoch) stale |= 1u << k;
               if (!stale) break;
               if ((it & 15) == 15) {
-                if (*(volatile int*)&D.sh->abort) break;
+                if (abort_seen(D)) break;
                 if (__hip_atomic_load(&D.state[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
-                  D.sh->abort = 1;
+                  set_abort(D);
                   break;
                 }
                 if (wall_clock64() - t0 > D.p->timeout_ticks) {
@@ -1367,19 +1401,12 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
           for (int w = 0; w < kWaves; ++w) y += part[t * kWaves + w];
           const int row = r0 + t;
           if (p.logits) p.logits[(uint64_t)out_step * V + row] = y;
-          if (y > my_val || (y == my_val && row < my_idx)) {
+          if (argmax_better(y, row, my_val, my_idx)) {
             my_val = y;
             my_idx = row;
           }
         }
-        for (int off = 32; off >= 1; off >>= 1) {
-          const float ov = __shfl_xor(my_val, off);
-          const int oi = __shfl_xor(my_idx, off);
-          if (ov > my_val || (ov == my_val && oi < my_idx)) {
-            my_val = ov;
-            my_idx = oi;
-          }
-        }
+        wave_argmax(my_val, my_idx);
         if (D.lane == 0) {
           D.sh->lmv[D.wave] = my_val;
           D.sh->lmi[D.wave] = my_idx;
@@ -1407,7 +1434,7 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
         for (int w = 1; w < kWaves; ++w) {
           const float ov = D.sh->lmv[w];
           const int oi = D.sh->lmi[w];
-          if (ov > bv || (ov == bv && oi < bi)) {
+          if (argmax_better(ov, oi, bv, bi)) {
             bv = ov;
             bi = oi;
           }
@@ -1416,14 +1443,27 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
       ll_storef(D.LMP + 2 * D.wg, bv, epoch);
       ll_store(D.LMP + 2 * D.wg + 1, (uint32_t)bi, epoch);
     }
-    // every workgroup reads every partial and takes the same decision
-    float* lv = xs;
-    int* li = (int*)(xs + D.nwg);
-    for (int t = D.tid; t < D.nwg; t += kThreads) {
-      u64 ab[2];
-      poll_words<2>(D, D.LMP + 2 * t, 1, 3u, epoch, ab);
-      lv[t] = ll_f(ab[0]);
-      li[t] = (int)(uint32_t)ab[1];
+    // every workgroup reads every partial and takes the same decision: each
+    // thread keeps the best of the partials it polled, then each wave's best
+    // goes to LDS
+    {
+      float bv = -INFINITY;
+      int bi = 0x7FFFFFFF;
+      for (int t = D.tid; t < D.nwg; t += kThreads) {
+        u64 ab[2];
+        poll_words<2>(D, D.LMP + 2 * t, 1, 3u, epoch, ab);
+        const float ov = ll_f(ab[0]);
+        const int oi = (int)(uint32_t)ab[1];
+        if (argmax_better(ov, oi, bv, bi)) {
+          bv = ov;
+          bi = oi;
+        }
+      }
+      wave_argmax(bv, bi);
+      if (D.lane == 0) {
+        D.sh->tokv[D.wave] = bv;
+        D.sh->toki[D.wave] = bi;
+      }
     }
     wg_sync();
     // every workgroup's release is now observed: one acquire (L1 and L2
@@ -1436,19 +1476,19 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
     if (aborted(D)) { __builtin_amdgcn_s_waitcnt(kWaitAllVm); return; }
     stamp(D, s, tph, 1);
     if (lm) {
-      if (D.tid == 0) {
-        float bv = lv[0];
-        int bi = li[0];
-        for (int t = 1; t < D.nwg; ++t) {
-          if (lv[t] > bv || (lv[t] == bv && li[t] < bi)) {
-            bv = lv[t];
-            bi = li[t];
-          }
+      // every thread reduces the eight wave results the same way
+      float bv = D.sh->tokv[0];
+      int bi = D.sh->toki[0];
+#pragma unroll
+      for (int w = 1; w < kWaves; ++w) {
+        const float ov = D.sh->tokv[w];
+        const int oi = D.sh->toki[w];
+        if (argmax_better(ov, oi, bv, bi)) {
+          bv = ov;
+          bi = oi;
         }
-        D.sh->token = bi;
       }
-      wg_sync();
-      token = D.sh->token;
+      token = rfl(bi);
       if (D.wg == 0 && D.tid == 0) {
         if (p.out) p.out[p.lm_mode == 1 ? 0 : s] = token;
         D.state[2] = token;
