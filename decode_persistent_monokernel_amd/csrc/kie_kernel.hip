@@ -579,6 +579,42 @@ KIE_DI void cursor_issue4(const Dev& D, Cursor& c, int slot) {
   }
 }
 
+// Refills owed by the attention stream.  Once the cursor has left the
+// attention chunks, the attention stream stops refilling the slots it frees:
+// those loads (the next phase's first weights) would queue in front of the
+// merger's record poll and the next prologue's poll (a wave's loads complete
+// in issue order), and issuing them while the memory pipeline is full would
+// stall the attention arithmetic itself.  They are issued after the
+// attention records are out, into the consecutive slots from `slot`.
+struct Owed {
+  int n, slot;
+};
+// refill the k freed slots from `slot` on: attention chunks while the
+// cursor still has some (it is not advanced here), the rest owed
+KIE_DI void attn_refill(const Dev& D, Cursor& c, int slot, int k, Owed& o) {
+  int i = 0;
+  if (o.n == 0 && c.attn && !c.done) {
+#pragma unroll 1
+    for (; i < k && c.rem > 0; ++i) {
+      dma_chunk(D, c.base + (c.kvh ? c.voff : 0), ring_add(slot, i));
+      if (c.kvh) c.base += c.stride;
+      c.kvh ^= 1;
+      --c.rem;
+    }
+  }
+  if (i < k) {
+    if (o.n == 0) o.slot = ring_add(slot, i);
+    o.n += k - i;
+  }
+}
+KIE_DI void issue_owed(const Dev& D, Cursor& c, Owed& o) {
+  make_uniform(c, o.slot);
+  o.n = rfl(o.n);
+#pragma unroll 1
+  for (int i = 0; i < o.n; ++i) cursor_issue(D, c, ring_add(o.slot, i));
+  o.n = 0;
+}
+
 typedef float f4v __attribute__((ext_vector_type(4)));
 typedef unsigned u4v __attribute__((ext_vector_type(4)));
 
@@ -757,29 +793,42 @@ KIE_DI void attn_step(const Dev& D, const u4v kx, const u4v vx, int key, int kc,
 }
 
 template <int G>
-KIE_DI void attn_stream(const Dev& D, Cursor& cur, int& slot, int nst, int ka, int kc, const float (&q)[G][8],
-                        float (&mrow)[G], float (&lrow)[G], float (&acc)[G][8]) {
+KIE_DI void attn_stream(const Dev& D, Cursor& cur, int& slot, Owed& owed, int nst, int ka, int kc,
+                        const float (&q)[G][8], float (&mrow)[G], float (&lrow)[G], float (&acc)[G][8]) {
   make_uniform(cur, slot);
   int st = 0;
   for (; st + 2 <= nst; st += 2) {
     uint32_t ra[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) ra[k] = ring_addr(D, ring_add(slot, k));
-    __builtin_amdgcn_s_waitcnt(kWaitRing4);
+    // with refills owed fewer loads are in flight than the ring holds, so
+    // the usual count no longer marks these slots: wait for all of them
+    if (rfl(owed.n) == 0) {
+      __builtin_amdgcn_s_waitcnt(kWaitRing4);
+    } else {
+      __builtin_amdgcn_s_waitcnt(kWaitAllVm);
+    }
     u4v x[4];
     read_kv2(ra, x);
-    cursor_issue4(D, cur, slot);
+    if (owed.n == 0 && cur.attn && !cur.done && cur.rem >= 4 && cur.kvh == 0) {
+      cursor_issue4(D, cur, slot);
+    } else {
+      attn_refill(D, cur, slot, 4, owed);
+    }
     slot = ring_add(slot, 4);
     attn_step<G>(D, x[0], x[1], ka + st * D.kpl + D.kl, kc, q, mrow, lrow, acc);
     attn_step<G>(D, x[2], x[3], ka + (st + 1) * D.kpl + D.kl, kc, q, mrow, lrow, acc);
   }
   if (st < nst) {
-    __builtin_amdgcn_s_waitcnt(kWaitRing2);
+    if (rfl(owed.n) == 0) {
+      __builtin_amdgcn_s_waitcnt(kWaitRing2);
+    } else {
+      __builtin_amdgcn_s_waitcnt(kWaitAllVm);
+    }
     const int sv = ring_next(slot);
     u4v kx, vx;
     read_kv(ring_addr(D, slot), ring_addr(D, sv), kx, vx);
-#pragma unroll 1
-    for (int k = 0; k < 2; ++k) cursor_issue(D, cur, ring_add(slot, k));
+    attn_refill(D, cur, slot, 2, owed);
     slot = ring_next(sv);
     attn_step<G>(D, kx, vx, ka + st * D.kpl + D.kl, kc, q, mrow, lrow, acc);
   }
@@ -1010,6 +1059,7 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
         // ================= attention over the KV cache ==================
         float mrow[G], lrow[G], acc[G][8], q[G][8];
         const int nseg = rfl(adesc[10]);
+        Owed owed{0, 0};
         // The query heads of every segment and the key and value at the
         // current position (all written by this step's QKV epilogue), polled
         // once by the whole workgroup into LDS: qkv[sg][G + 2][hd].  No wave
@@ -1058,7 +1108,7 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
           for (int h = 0; h < G; ++h)
 #pragma unroll
             for (int e = 0; e < 8; ++e) q[h][e] = qs[h * hd + e];
-          attn_stream<G>(D, cur, slot, nst, ka, kc, q, mrow, lrow, acc);
+          attn_stream<G>(D, cur, slot, owed, nst, ka, kc, q, mrow, lrow, acc);
           if (has_pos) {
             // current key and value (fp16-rounded by the QKV epilogue)
             float kx[8], vx[8];
@@ -1241,6 +1291,8 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
             ll_storef(D.OB + (uint64_t)l * qd + (uint64_t)(g * G + h) * hd + dd, o, epoch);
           }
         }
+        // the records (and a merger's output) are out: now the deferred loads
+        issue_owed(D, cur, owed);
         wg_sync();
         if (aborted(D)) { __builtin_amdgcn_s_waitcnt(kWaitAllVm); return; }
         stamp(D, s, ph, 3);
