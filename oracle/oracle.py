@@ -27,7 +27,9 @@ Pins (tests/test_oracle_pins.py): brute-force scalar loops on tiny shapes,
 KV-cached decode == no-cache recomputation, RoPE closed forms and the
 relative-position identity, single-key attention returns V, softmax rows sum
 to 1, GQA == MHA with duplicated KV heads, lane partials sum to the unsplit
-layer, delay 0 == parallel block, argmax ties.  End-to-end logits of a model
+layer, delay 0 == parallel block, argmax ties; for sampling, the published
+Philox4x32-10 known-answer vectors, Gumbel-max frequencies against
+softmax(logits / T) by a chi-square test, and T -> 0 reducing to greedy.  End-to-end logits of a model
 are "parity unpinned" against the pages: they print no logits or tokens.
 """
 from __future__ import annotations
@@ -88,6 +90,71 @@ def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray) -> np.ndarray:
 def greedy(logits: np.ndarray) -> int:
     """lowest id among exact maxima"""
     return int(np.argmax(logits))
+
+
+# --------------------------------------------------------------------------
+# stochastic LM-head sampling
+# --------------------------------------------------------------------------
+# The pages (Kog explainer, "Monokernel" section) place LM-head sampling inside
+# the persistent kernel but do not say which sampler.  The reading used here:
+# temperature sampling drawn with the Gumbel-max property (argmax of
+# logits / T plus independent standard Gumbel noise is distributed as
+# softmax(logits / T)), the noise taken from the counter-based generator
+# Philox4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as
+# easy as 1, 2, 3", SC 2011) keyed by the 64-bit seed, with counter
+# (vocabulary row, position, 0, 0).  T = 0 is greedy decoding.
+PHILOX_M = (0xD2511F53, 0xCD9E8D57)  # round multipliers
+PHILOX_W = (0x9E3779B9, 0xBB67AE85)  # key increments between rounds
+
+
+def philox4x32(counter, key, rounds: int = 10):
+    """Philox4x32 with `rounds` rounds, elementwise over uint32 arrays.
+
+    counter: four arrays (or ints) c0..c3; key: two ints k0, k1.  One round
+    multiplies c0 and c2 by the two constants into 64-bit products and forms
+    (hi(c2*M1) ^ c1 ^ k0, lo(c2*M1), hi(c0*M0) ^ c3 ^ k1, lo(c0*M0)); the key
+    advances by the two Weyl increments after every round.  Returns the four
+    output words as uint64 arrays holding 32-bit values."""
+    m32 = np.uint64(0xFFFFFFFF)
+    c = [np.asarray(x, dtype=np.uint64) & m32 for x in counter]
+    k0, k1 = int(key[0]) & 0xFFFFFFFF, int(key[1]) & 0xFFFFFFFF
+    for _ in range(rounds):
+        p0 = np.uint64(PHILOX_M[0]) * c[0]
+        p1 = np.uint64(PHILOX_M[1]) * c[2]
+        c = [(p1 >> np.uint64(32)) ^ c[1] ^ np.uint64(k0), p1 & m32,
+             (p0 >> np.uint64(32)) ^ c[3] ^ np.uint64(k1), p0 & m32]
+        k0 = (k0 + PHILOX_W[0]) & 0xFFFFFFFF
+        k1 = (k1 + PHILOX_W[1]) & 0xFFFFFFFF
+    return c
+
+
+def uniform_open(words: np.ndarray) -> np.ndarray:
+    """(0, 1) from 32-bit words: the top 23 bits plus one half, times 2^-23
+    (exact in float32 as well)"""
+    return ((np.asarray(words, dtype=np.uint64) >> np.uint64(9)).astype(f64) + 0.5) * 2.0 ** -23
+
+
+def gumbel_noise(seed: int, pos: int, n: int) -> np.ndarray:
+    """standard Gumbel noise -log(-log(u)) for rows 0..n-1 at position pos"""
+    rows = np.arange(n, dtype=np.uint64)
+    w0 = philox4x32((rows, np.full(n, pos, np.uint64), 0, 0), (seed & 0xFFFFFFFF, seed >> 32))[0]
+    return -np.log(-np.log(uniform_open(w0)))
+
+
+def sample(logits: np.ndarray, temperature: float, seed: int, pos: int) -> int:
+    """the token emitted after position pos: greedy for T = 0, else argmax of
+    logits / T + Gumbel noise (lowest id among exact maxima)"""
+    if temperature == 0:
+        return greedy(logits)
+    z = np.asarray(logits, dtype=f64) / f64(temperature) + gumbel_noise(seed, pos, len(logits))
+    return int(np.argmax(z))
+
+
+def sampling_scores(logits: np.ndarray, temperature: float, seed: int, pos: int) -> np.ndarray:
+    """the perturbed scores whose argmax `sample` takes"""
+    if temperature == 0:
+        return np.asarray(logits, dtype=f64)
+    return np.asarray(logits, dtype=f64) / f64(temperature) + gumbel_noise(seed, pos, len(logits))
 
 
 # --------------------------------------------------------------------------
@@ -264,20 +331,23 @@ class Oracle:
 
     # -- runs ---------------------------------------------------------------
     def run(self, prompt: Sequence[int], n_steps: int,
-            forced: Optional[Sequence[int]] = None, keep_logits: bool = True):
+            forced: Optional[Sequence[int]] = None, keep_logits: bool = True,
+            temperature: float = 0.0, seed: int = 0):
         """Prefill `prompt`, then n_steps decode steps.  Step k consumes
-        forced[k] if given, else the previous argmax (t1 from the prefill for
-        k = 0), runs at position len(prompt) + k and emits argmax.
+        forced[k] if given, else the previous emitted token (t1 from the
+        prefill for k = 0), runs at position len(prompt) + k and emits
+        sample(logits, temperature, seed, position) (argmax for T = 0; t1 is
+        drawn at position len(prompt) - 1).
         Returns dict(t1, prefill_logits, inputs, tokens, logits)."""
         P = len(prompt)
         cache = self.new_cache(P + n_steps)
         lg0 = self.prefill(cache, prompt)
-        t = greedy(lg0)
+        t = sample(lg0, temperature, seed, P - 1)
         res = dict(t1=t, prefill_logits=lg0, inputs=[], tokens=[], logits=[])
         for k in range(n_steps):
             tin = int(forced[k]) if forced is not None else t
             lg = self.step(cache, tin, P + k)
-            t = greedy(lg)
+            t = sample(lg, temperature, seed, P + k)
             res["inputs"].append(tin)
             res["tokens"].append(t)
             if keep_logits:

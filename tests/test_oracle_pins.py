@@ -403,3 +403,86 @@ def test_planted_mlp_mistakes_are_caught(monkeypatch):
     assert _caught(monkeypatch, **{"Oracle.mlp": swapped})
     transposed = lambda self, L, h: (O.silu(h @ L.w_gate.T) * (h @ L.w_up.T)) @ L.w_down.T * 1.0001
     assert _caught(monkeypatch, **{"Oracle.mlp": transposed})
+
+
+# --------------------------------------------------------------------------
+# stochastic LM-head sampling (the oracle's reading: Gumbel-max over
+# Philox4x32-10 noise)
+# --------------------------------------------------------------------------
+# Known-answer vectors of Philox4x32 with 10 rounds as published with the
+# generator (Salmon et al., "Parallel random numbers: as easy as 1, 2, 3",
+# SC 2011, and its reference implementation's test vectors): counter, key,
+# output words.
+PHILOX_KAT = [
+    ((0x00000000, 0x00000000, 0x00000000, 0x00000000), (0x00000000, 0x00000000),
+     (0x6627e8d5, 0xe169c58d, 0xbc57ac4c, 0x9b00dbd8)),
+    ((0xffffffff, 0xffffffff, 0xffffffff, 0xffffffff), (0xffffffff, 0xffffffff),
+     (0x408f276d, 0x41c83b0e, 0xa20bc7c6, 0x6d5451fd)),
+    ((0x243f6a88, 0x85a308d3, 0x13198a2e, 0x03707344), (0xa4093822, 0x299f31d0),
+     (0xd16cfe09, 0x94fdcceb, 0x5001e420, 0x24126ea1)),
+]
+
+
+@pytest.mark.parametrize("ctr,key,want", PHILOX_KAT)
+def test_philox_known_answers(ctr, key, want):
+    got = O.philox4x32(ctr, key)
+    assert tuple(int(x) for x in got) == want
+
+
+def test_philox_is_elementwise_over_counters():
+    # a vector of counters gives, word for word, the scalar results
+    c0 = np.array([0, 0xffffffff, 0x243f6a88], dtype=np.uint64)
+    rows = [O.philox4x32((int(c), 7, 9, 11), (3, 5)) for c in c0]
+    vec = O.philox4x32((c0, 7, 9, 11), (3, 5))
+    for i in range(3):
+        assert [int(w[i]) for w in vec] == [int(w) for w in rows[i]]
+
+
+def test_uniform_is_open_and_exact():
+    u = O.uniform_open(np.array([0, 0xffffffff, 1 << 31], dtype=np.uint64))
+    assert u[0] == 0.5 * 2.0 ** -23 and u[1] == 1 - 0.5 * 2.0 ** -23 and u[2] == 0.5 + 0.5 * 2.0 ** -23
+    assert np.all(u.astype(np.float32).astype(np.float64) == u)  # representable in float32
+
+
+def test_gumbel_max_matches_softmax_chi_square():
+    # the oracle's sampler over many independent draws (positions 0..N-1 of
+    # one seed) follows softmax(l/T): chi-square with 5 degrees of freedom
+    l = np.array([1.3, 0.2, -0.5, 2.0, 1.9, -1.0])
+    T, N = 0.7, 20000
+    seed = 0x1234_5678_9abc
+    picks = np.array([O.sample(l, T, seed, k) for k in range(N)])
+    counts = np.bincount(picks, minlength=len(l))
+    p = O.softmax(l / T)
+    chi2 = float(np.sum((counts - N * p) ** 2 / (N * p)))
+    assert chi2 < 25.7, (chi2, counts, N * p)  # 25.7 = chi-square(5) upper 1e-4 point
+
+
+def test_sampling_low_temperature_is_greedy_and_zero_is_greedy():
+    rng = np.random.default_rng(5)
+    for _ in range(20):
+        l = rng.normal(size=50)
+        assert O.sample(l, 0.0, 99, 3) == O.greedy(l)
+        # Gumbel noise is bounded by ~ -log(-log(1 - 2^-24)) < 17, so a
+        # temperature that scales the top-2 gap above 40 cannot flip it
+        s = np.sort(l)
+        T = (s[-1] - s[-2]) / 40
+        assert O.sample(l, T, 99, 3) == O.greedy(l)
+
+
+def test_sampling_streams_differ_by_position_and_seed():
+    a = O.gumbel_noise(1, 10, 64)
+    assert not np.array_equal(a, O.gumbel_noise(1, 11, 64))
+    assert not np.array_equal(a, O.gumbel_noise(2, 10, 64))
+    assert not np.array_equal(a, O.gumbel_noise(1 << 32 | 1, 10, 64))  # the seed's upper half counts
+    assert np.array_equal(a, O.gumbel_noise(1, 10, 64))
+
+
+def test_planted_gumbel_sign_mistake_is_caught(monkeypatch):
+    # +log(-log(u)) instead of -log(-log(u)): the chi-square pin must fail
+    def wrong(seed, pos, n):
+        rows = np.arange(n, dtype=np.uint64)
+        w0 = O.philox4x32((rows, np.full(n, pos, np.uint64), 0, 0), (seed & 0xFFFFFFFF, seed >> 32))[0]
+        return np.log(-np.log(O.uniform_open(w0)))
+    monkeypatch.setattr(O, "gumbel_noise", wrong)
+    with pytest.raises(AssertionError):
+        test_gumbel_max_matches_softmax_chi_square()
