@@ -34,6 +34,8 @@ struct kie_ctx {
   uint32_t next_epoch = 1;  // epoch of the next decode step (0 = never written)
   uint64_t timeout_us = 2000000;
   uint32_t debug = 0;
+  float temperature = 0.f;  // 0: greedy
+  uint64_t seed = 0;
   int32_t launch_steps = 512;
   uint64_t* trace = nullptr;
   int32_t trace_steps = 0;
@@ -190,6 +192,10 @@ kie::KParams base_params(const kie_ctx* c) {
   kp.debug_flags = c->debug;
   kp.trace = c->trace;
   kp.trace_steps = c->trace_steps;
+  kp.sample = c->temperature > 0.f ? 1 : 0;
+  kp.inv_temp = c->temperature > 0.f ? 1.0f / c->temperature : 1.0f;
+  kp.seed_lo = (uint32_t)c->seed;
+  kp.seed_hi = (uint32_t)(c->seed >> 32);
   return kp;
 }
 
@@ -416,6 +422,15 @@ kie_status kie_sync_status(kie_ctx* c, void* stream) {
 kie_status kie_set_timeout_us(kie_ctx* c, uint64_t us) {
   if (!c || us == 0) return KIE_ERR_INVALID_ARG;
   c->timeout_us = us;
+  return KIE_OK;
+}
+
+kie_status kie_set_sampling(kie_ctx* c, float temperature, uint64_t seed) {
+  if (!c) return KIE_ERR_INVALID_ARG;
+  if (!std::isfinite(temperature) || temperature < 0.f)
+    return fail(c, KIE_ERR_INVALID_ARG, "temperature must be finite and >= 0 (0 = greedy)");
+  c->temperature = temperature;
+  c->seed = seed;
   return KIE_OK;
 }
 

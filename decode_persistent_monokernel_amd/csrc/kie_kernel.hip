@@ -82,6 +82,30 @@ KIE_DI float wave_max(float v) {
   return v;
 }
 // sum over groups of `lpk` consecutive lanes; every lane of a group gets it
+// Philox4x32-10 (Salmon, Moraes, Dror and Shaw, SC 2011), first output word
+// for counter (c0, c1, 0, 0) and key (k0, k1): ten rounds of two 32x32->64
+// products, the key advanced by the two Weyl increments after each round
+KIE_DI uint32_t philox_w0(uint32_t c0, uint32_t c1, uint32_t k0, uint32_t k1) {
+  uint32_t c2 = 0, c3 = 0;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint32_t lo0 = 0xD2511F53u * c0, hi0 = __umulhi(0xD2511F53u, c0);
+    const uint32_t lo1 = 0xCD9E8D57u * c2, hi1 = __umulhi(0xCD9E8D57u, c2);
+    c0 = hi1 ^ c1 ^ k0;
+    c1 = lo1;
+    c2 = hi0 ^ c3 ^ k1;
+    c3 = lo0;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return c0;
+}
+// standard Gumbel noise -log(-log(u)), u = (top 23 bits + 1/2) * 2^-23 in (0, 1)
+KIE_DI float gumbel(uint32_t w) {
+  const float u = ((float)(w >> 9) + 0.5f) * 0x1p-23f;
+  return -logf(-logf(u));
+}
+
 // greedy order: the larger value wins, equal values go to the smaller index
 KIE_DI bool argmax_better(float ov, int oi, float bv, int bi) { return ov > bv || (ov == bv && oi < bi); }
 KIE_DI void wave_argmax(float& v, int& i) {
@@ -1453,8 +1477,11 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
           for (int w = 0; w < kWaves; ++w) y += part[t * kWaves + w];
           const int row = r0 + t;
           if (p.logits) p.logits[(uint64_t)out_step * V + row] = y;
-          if (argmax_better(y, row, my_val, my_idx)) {
-            my_val = y;
+          // sampling: the Gumbel-max draw over logits / T
+          const float sc = p.sample ? y * p.inv_temp + gumbel(philox_w0((uint32_t)row, (uint32_t)pos, p.seed_lo, p.seed_hi))
+                                    : y;
+          if (argmax_better(sc, row, my_val, my_idx)) {
+            my_val = sc;
             my_idx = row;
           }
         }

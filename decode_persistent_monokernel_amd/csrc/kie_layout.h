@@ -364,6 +364,12 @@ struct KParams {
   // end) at trace[((step * kTracePhases + phase) * nwg + wg) * 4]
   uint64_t* trace;
   int trace_steps;
+  // stochastic LM-head sampling (sample != 0): the token is the argmax of
+  // logits * inv_temp + Gumbel noise from Philox4x32-10 keyed by
+  // (seed_lo, seed_hi) at counter (row, position, 0, 0)
+  int sample;
+  float inv_temp;
+  uint32_t seed_lo, seed_hi;
 };
 constexpr int kTracePhases = 5 * 64 + 2;  // up to 64 layers, LM, step end
 

@@ -68,6 +68,7 @@ def lib() -> C.CDLL:
         L.kie_sync_status.argtypes = [vp, vp]
         L.kie_set_timeout_us.argtypes = [vp, C.c_uint64]
         L.kie_set_debug_flags.argtypes = [vp, C.c_uint32]
+        L.kie_set_sampling.argtypes = [vp, C.c_float, C.c_uint64]
         L.kie_set_launch_steps.argtypes = [vp, i32]
         L.kie_set_trace.argtypes = [vp, vp, i32]
         L.kie_pack_weights_host.argtypes = [C.POINTER(ModelConfigC), C.POINTER(WeightsC), vp]
@@ -84,7 +85,8 @@ def lib() -> C.CDLL:
         L.kie_destroy.restype = None
         for name in ("kie_create", "kie_query_sizes", "kie_bind_memory", "kie_load_weights",
                      "kie_prefill", "kie_decode", "kie_set_position", "kie_sync_status",
-                     "kie_set_timeout_us", "kie_set_debug_flags", "kie_set_launch_steps", "kie_set_trace",
+                     "kie_set_timeout_us", "kie_set_debug_flags", "kie_set_sampling", "kie_set_launch_steps",
+                     "kie_set_trace",
                      "kie_pack_weights_host", "kie_launch_info", "kie_validate_schedule"):
             getattr(L, name).restype = C.c_int
         _lib = L
@@ -225,6 +227,11 @@ class Engine:
 
     def set_debug_flags(self, flags: int):
         _check(self.L.kie_set_debug_flags(self.ctx, int(flags)), self.ctx)
+
+    def set_sampling(self, temperature: float, seed: int = 0):
+        """kie_set_sampling: temperature 0 is greedy; else Gumbel-max draws
+        from softmax(logits / temperature) with Philox noise keyed by seed"""
+        _check(self.L.kie_set_sampling(self.ctx, float(temperature), int(seed) & 0xFFFFFFFFFFFFFFFF), self.ctx)
 
     TRACE_PHASES = 5 * 64 + 2
 

@@ -135,7 +135,7 @@ kie_status kie_prefill(kie_ctx* ctx, const int32_t* d_prompt, int32_t n_prompt, 
 /* Run n_tokens decode steps.  Step k consumes d_forced_in[k] when that
  * pointer is not NULL (teacher forcing), else the previous step's argmax (the
  * pending token for k = 0); it runs at position pos + k, writes its greedy
- * token to d_tokens_out[k] (device, may be NULL) and, when d_logits_out is not
+ * (or sampled, see kie_set_sampling) token to d_tokens_out[k] (device, may be NULL) and, when d_logits_out is not
  * NULL, its logits to d_logits_out[k*vocab .. (k+1)*vocab).  Afterwards
  * position += n_tokens and the last emitted token is pending.
  * KIE_ERR_CAPACITY if position + n_tokens > max_ctx. */
@@ -157,6 +157,21 @@ kie_status kie_sync_status(kie_ctx* ctx, void* stream);
 /* Longest time one wait inside the kernel may take before the launch gives
  * up with KIE_ERR_TIMEOUT (default 2 000 000 us). */
 kie_status kie_set_timeout_us(kie_ctx* ctx, uint64_t microseconds);
+
+/* Stochastic LM-head sampling inside the kernel (Kog explainer, "Monokernel"
+ * section: LM-head sampling runs in the persistent kernel; the sampler is
+ * not named there).  For temperature T > 0 every emitted token -- the
+ * prefill's t1 and each decode step's -- is the argmax over vocabulary rows i
+ * of logits[i] / T + g_i, where g_i = -log(-log(u_i)) is standard Gumbel
+ * noise, so the token is a draw from softmax(logits / T).  u_i = ((w >> 9) +
+ * 1/2) * 2^-23 with w the first output word of Philox4x32-10 (Salmon et al.,
+ * SC 2011) with key (seed mod 2^32, seed >> 32) and counter (i, position,
+ * 0, 0), where position is that of the input token the logits follow from.
+ * Equal scores go to the lower id.  T = 0 (the default) is greedy decoding.
+ * Logits written to d_logits / d_logits_out stay unperturbed.  Applies to
+ * later kie_prefill and kie_decode calls; KIE_ERR_INVALID_ARG for a negative
+ * or non-finite temperature (the setting is then left unchanged). */
+kie_status kie_set_sampling(kie_ctx* ctx, float temperature, uint64_t seed);
 
 /* Debug flags (bit 0: one workgroup waits on a word nobody writes, which
  * must end in KIE_ERR_TIMEOUT, not a hang).  0 = normal operation. */

@@ -82,6 +82,12 @@ def test_host_only_context_refuses_gpu_calls():
         assert L.kie_prefill(ctx, 256, 1, None, None, None) == -4
         assert L.kie_set_timeout_us(ctx, 0) == -1
         assert L.kie_set_launch_steps(ctx, 0) == -1
+        # sampling settings are host state: checked without a GPU
+        assert L.kie_set_sampling(ctx, -0.5, 1) == -1
+        assert L.kie_set_sampling(ctx, float("nan"), 1) == -1
+        assert L.kie_set_sampling(ctx, float("inf"), 1) == -1
+        assert L.kie_set_sampling(ctx, 0.0, 0) == 0
+        assert L.kie_set_sampling(ctx, 0.8, 2**64 - 1) == 0
         assert L.kie_position(ctx) == 0
         assert L.kie_status_string(-5) == b"wait timed out inside the kernel"
     finally:
