@@ -1,7 +1,7 @@
 """Compile the HIP library in-tree for gfx950.
 
-libkie.so = the persistent decode kernel (kie_kernel.hip) + the host C ABI
-(kie_api.cpp).  Built with hipcc; packed fp32 vector instructions are turned
+libkie.so = the persistent decode kernel (kie_kernel.hip) + the batched
+prefill kernels (kie_prefill.hip) + the host C ABI (kie_api.cpp).  Built with hipcc; packed fp32 vector instructions are turned
 off for the device code (-packed-fp32-ops).
 """
 from __future__ import annotations
@@ -45,6 +45,9 @@ def build(verbose: bool = False) -> str:
     k_o = os.path.join(tmp, "kie_kernel.o")
     _run([cc, f"--offload-arch={ARCH}", *common, *dev, "-c", os.path.join(CSRC, "kie_kernel.hip"), "-o", k_o], verbose)
     objs.append(k_o)
+    p_o = os.path.join(tmp, "kie_prefill.o")
+    _run([cc, f"--offload-arch={ARCH}", *common, *dev, "-c", os.path.join(CSRC, "kie_prefill.hip"), "-o", p_o], verbose)
+    objs.append(p_o)
     a_o = os.path.join(tmp, "kie_api.o")
     _run([cc, *common, "-c", os.path.join(CSRC, "kie_api.cpp"), "-o", a_o], verbose)
     objs.append(a_o)

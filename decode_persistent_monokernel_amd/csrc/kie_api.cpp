@@ -16,6 +16,7 @@
 extern "C" hipError_t kie_internal_launch(const kie::KParams* kp, int nwg, size_t lds_bytes, hipStream_t stream);
 extern "C" hipError_t kie_internal_zero(void* p, size_t bytes, hipStream_t stream);
 extern "C" hipError_t kie_internal_occupancy(int G, size_t lds_bytes, int* blocks_per_cu);
+extern "C" hipError_t kie_internal_prefill_chunk(const kie::PrefillArgs* a, hipStream_t stream);
 
 struct kie_ctx {
   kie_model_config cfg;
@@ -44,6 +45,8 @@ struct kie_ctx {
 };
 
 namespace {
+
+constexpr int32_t kPrefillChunk = 1024;  // most prompt tokens per batched-prefill chunk
 
 kie_status fail(kie_ctx* c, kie_status s, const std::string& msg) {
   if (c) c->err = msg;
@@ -356,6 +359,52 @@ kie_status kie_prefill(kie_ctx* c, const int32_t* d_prompt, int32_t n, int32_t* 
     off += chunk;
   }
   return KIE_OK;
+}
+
+kie_status kie_prefill_scratch_bytes(const kie_ctx* c, int32_t chunk_tokens, size_t* bytes) {
+  if (!c || !bytes || chunk_tokens <= 0) return KIE_ERR_INVALID_ARG;
+  *bytes = (size_t)chunk_tokens * kie::pf_floats_per_token(c->m) * sizeof(float);
+  return KIE_OK;
+}
+
+kie_status kie_prefill_batched(kie_ctx* c, const int32_t* d_prompt, int32_t n, int32_t* d_next, float* d_logits,
+                               void* d_scratch, size_t scratch_bytes, void* stream) {
+  kie_status s = ready(c);
+  if (s != KIE_OK) return s;
+  if (!d_prompt || n <= 0) return fail(c, KIE_ERR_INVALID_ARG, "empty prompt");
+  if ((int64_t)c->pos + n > c->m.max_ctx) return fail(c, KIE_ERR_CAPACITY, "prompt exceeds max_ctx");
+  // the lane-structured block, and shapes the batched kernels do not take,
+  // run token by token; so does a one-token prompt
+  const bool batched = !c->m.parallel && n > 1 && c->m.hd <= 512 && (c->m.hd % 8) == 0 && (c->m.F % 4) == 0;
+  if (!batched) return kie_prefill(c, d_prompt, n, d_next, d_logits, stream);
+  if (!d_scratch || ((uintptr_t)d_scratch & 15))
+    return fail(c, KIE_ERR_INVALID_ARG, "prefill scratch must be a 16-byte aligned device buffer");
+  const uint64_t per_token = kie::pf_floats_per_token(c->m) * sizeof(float);
+  const int64_t fit = (int64_t)(scratch_bytes / per_token);
+  if (fit < 1) return fail(c, KIE_ERR_INVALID_ARG, "prefill scratch holds less than one token (kie_prefill_scratch_bytes)");
+  const int32_t cmax = (int32_t)std::min<int64_t>(fit, kPrefillChunk);
+  hipStream_t st = (hipStream_t)stream;
+  kie::PrefillArgs a{};
+  a.m = c->m;
+  a.pl = c->pl;
+  a.W = (const uint16_t*)c->packed;
+  a.kv = (uint16_t*)c->kv;
+  a.rope = (const float2*)((uint8_t*)c->ws + c->wl.rope);
+  a.state = (int32_t*)((uint8_t*)c->ws + c->wl.state);
+  a.scratch = (float*)d_scratch;
+  for (int32_t off = 0; off < n - 1;) {
+    const int32_t C = std::min<int32_t>(cmax, n - 1 - off);
+    a.tokens = d_prompt + off;
+    a.C = C;
+    a.pos0 = c->pos + off;
+    const hipError_t e = kie_internal_prefill_chunk(&a, st);
+    if (e != hipSuccess) return hip_fail(c, e, "batched prefill launch");
+    off += C;
+  }
+  c->pos += n - 1;
+  // the last prompt token goes through the decode kernel: LM head, the
+  // greedy or sampled t1, its logits, and the pending-token state
+  return kie_prefill(c, d_prompt + n - 1, 1, d_next, d_logits, stream);
 }
 
 kie_status kie_decode(kie_ctx* c, int32_t n, int32_t* d_out, const int32_t* d_forced, float* d_logits,

@@ -373,6 +373,35 @@ struct KParams {
 };
 constexpr int kTracePhases = 5 * 64 + 2;  // up to 64 layers, LM, step end
 
+// Batched prefill of prompt tokens [0, C) of one chunk (all but the prompt's
+// last token go this way; the last one runs through the decode kernel).  The
+// chunk's activations live in caller scratch, fp32, token-major:
+//   X  [C][d]                residual stream
+//   Y  [C][max(d, F)]        RMSNorm output, then the SwiGLU activations
+//   Gb [C][max(qd+2kvd, 2F)] QKV or gate/up GEMM output (packed row order)
+//   Qn [C][qd]               rotated queries, scaled by log2(e)/sqrt(hd)
+//   Ao [C][qd]               attention output (natural head-major order)
+struct PrefillArgs {
+  Dims m;
+  PackLayout pl;
+  const uint16_t* W;     // packed weights
+  uint16_t* kv;          // KV cache
+  const float2* rope;    // [max_ctx][hd/2] (cos, sin)
+  int32_t* state;        // device status words (bad token -> DEV_BAD_TOKEN)
+  const int32_t* tokens; // [C] device ids of this chunk
+  int C, pos0;
+  float* scratch;
+};
+KIE_HD int pf_ycols(const Dims& m) { return m.d > m.F ? m.d : m.F; }
+KIE_HD int pf_gcols(const Dims& m) {
+  const int qkv = (m.H + 2 * m.Hkv) * m.hd;
+  return qkv > 2 * m.F ? qkv : 2 * m.F;
+}
+// fp32 scratch floats per prompt token of a chunk
+KIE_HD uint64_t pf_floats_per_token(const Dims& m) {
+  return (uint64_t)m.d + pf_ycols(m) + pf_gcols(m) + 2ull * m.H * m.hd;
+}
+
 enum DebugFlags : uint32_t {
   DBG_WAIT_NEVER = 1u,  // workgroup 0 waits on a word no one writes (timeout test)
 };

@@ -1,0 +1,356 @@
+// Batched prefill: the prompt's tokens (all but the last) pushed through the
+// layers a chunk of C tokens at a time, with the weight GEMMs on the matrix
+// cores.  The pages' monokernel runs prefill on the GPU as well (Kog
+// explainer, "Monokernel" section); batching the prompt turns its GEMVs into
+// dense [C x K] x [K x N] products, so each weight is read once per chunk
+// instead of once per token.
+//
+// Arithmetic matches the decode kernel's: fp32 activations, fp16 weights
+// widened exactly, fp32 accumulation (v_mfma_f32_32x32x2f32), the same RMSNorm,
+// RoPE, fp16 rounding of cached K and V, exp2-domain softmax and SwiGLU
+// formulas.  Only summation orders differ.
+//
+// Kernels, launched in stream order per chunk and layer:
+//   embed -> [rmsnorm -> gemm(QKV) -> rope_kv -> attention -> gemm(O, +X)
+//             -> rmsnorm -> gemm(gate/up) -> swiglu -> gemm(down, +X)] x L
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kie_layout.h"
+
+namespace kie {
+namespace pf {
+
+typedef float f16v __attribute__((ext_vector_type(16)));
+
+constexpr int kRowThreads = 256;
+
+__device__ __forceinline__ float h2f(uint16_t u) { return __half2float(__ushort_as_half(u)); }
+
+__device__ __forceinline__ float block_sum(float v, float* red) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  float t = 0.f;
+  for (int i = 0; i < (int)(blockDim.x >> 6); ++i) t += red[i];
+  __syncthreads();
+  return t;
+}
+
+// X[m][:] = E[token m]; an id outside [0, V) reads row 0 and latches
+// DEV_BAD_TOKEN in the status word, as in the decode kernel
+__global__ void __launch_bounds__(kRowThreads) embed(float* X, const uint16_t* W, uint64_t embed_off,
+                                                     const int32_t* tok, int d, int V, int32_t* state) {
+  const int m = blockIdx.x;
+  int t = tok[m];
+  if (t < 0 || t >= V) {
+    if (threadIdx.x == 0) atomicCAS(&state[0], 0, (int)DEV_BAD_TOKEN);
+    t = 0;
+  }
+  const uint16_t* e = W + embed_off + (uint64_t)t * d;
+  for (int i = threadIdx.x; i < d; i += blockDim.x) X[(uint64_t)m * d + i] = h2f(e[i]);
+}
+
+// Y[m][:] = g * x / sqrt(mean(x^2) + eps)
+__global__ void __launch_bounds__(kRowThreads) rmsnorm(float* Y, int ldy, const float* X, int d,
+                                                       const uint16_t* g, float eps) {
+  __shared__ float red[kRowThreads / 64];
+  const int m = blockIdx.x;
+  const float* x = X + (uint64_t)m * d;
+  float ss = 0.f;
+  for (int i = threadIdx.x; i < d; i += blockDim.x) ss += x[i] * x[i];
+  const float tot = block_sum(ss, red);
+  const float inv = 1.0f / sqrtf(tot / (float)d + eps);
+  for (int i = threadIdx.x; i < d; i += blockDim.x) Y[(uint64_t)m * ldy + i] = x[i] * inv * h2f(g[i]);
+}
+
+// Out[m][n] (+)= sum_k A[m][k] * W[n][k] for m < M, n < N.  W is a packed
+// matrix: row pairs, each cut into 256-column blocks of one 1 KB chunk (256
+// columns of row 2p, then the same columns of row 2p+1, zero past K).
+// Tile 64 (m) x 128 (n) x 32 (k) per workgroup of 4 waves; wave w owns
+// columns n0 + 32w .. +32 and both 32-row halves, two 32x32 accumulators.
+// The next k tile is fetched into registers while the current one is
+// multiplied from LDS (double-buffered).
+constexpr int BM = 64, BN = 128, BK = 32, LDP = BK + 1;
+
+template <bool ADD>
+__global__ void __launch_bounds__(256) gemm(float* Out, int ldo, const float* A, int lda, const uint16_t* Wm,
+                                            int M, int N, int K) {
+  __shared__ float As[2][BM][LDP];
+  __shared__ float Bs[2][BN][LDP];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  const int nkt = (K + BK - 1) / BK;
+  const int cb = col_blocks(K);
+  // loads of this thread: A rows ar and ar + 32, columns ak .. ak + 3;
+  // B row bn (packed), columns bk .. bk + 15
+  const int ar = tid >> 3, ak = (tid & 7) * 4;
+  const int bn = tid >> 1, bk = (tid & 1) * 16;
+  float4 ra[2];
+  uint4 rb[2];
+  auto fetch = [&](int kt) {
+    const int k0 = kt * BK;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int m = m0 + ar + 32 * h, k = k0 + ak;
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (m < M) {
+        const float* a = A + (uint64_t)m * lda + k;
+        if (k + 3 < K) {
+          v = *(const float4*)a;
+        } else {
+          v.x = k < K ? a[0] : 0.f;
+          v.y = k + 1 < K ? a[1] : 0.f;
+          v.z = k + 2 < K ? a[2] : 0.f;
+          v.w = 0.f;
+        }
+      }
+      ra[h] = v;
+    }
+    const int n = n0 + bn, k = k0 + bk;  // k + 15 < 256 * cb: the padded row holds it
+    if (n < N) {
+      const uint16_t* w = Wm + ((uint64_t)(n >> 1) * cb + (k >> 8)) * 512 + (n & 1) * 256 + (k & 255);
+      rb[0] = *(const uint4*)w;
+      rb[1] = *(const uint4*)(w + 8);
+    } else {
+      rb[0] = make_uint4(0, 0, 0, 0);
+      rb[1] = make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float* d = &As[buf][ar + 32 * h][ak];
+      d[0] = ra[h].x;
+      d[1] = ra[h].y;
+      d[2] = ra[h].z;
+      d[3] = ra[h].w;
+    }
+    float* d = &Bs[buf][bn][bk];
+    const uint32_t w[8] = {rb[0].x, rb[0].y, rb[0].z, rb[0].w, rb[1].x, rb[1].y, rb[1].z, rb[1].w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      d[2 * i] = h2f((uint16_t)(w[i] & 0xFFFF));
+      d[2 * i + 1] = h2f((uint16_t)(w[i] >> 16));
+    }
+  };
+  f16v acc[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+  fetch(0);
+  stash(0);
+  __syncthreads();
+  const int li = lane & 31, lk = lane >> 5;
+  for (int kt = 0; kt < nkt; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nkt) fetch(kt + 1);
+#pragma unroll
+    for (int kk = 0; kk < BK; kk += 2) {
+      const float b = Bs[buf][wave * 32 + li][kk + lk];
+      const float a0 = As[buf][li][kk + lk];
+      const float a1 = As[buf][32 + li][kk + lk];
+      acc[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b, acc[0], 0, 0, 0);
+      acc[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b, acc[1], 0, 0, 0);
+    }
+    if (kt + 1 < nkt) stash(buf ^ 1);
+    __syncthreads();
+  }
+  // accumulator layout of a 32x32 tile: lane l, element r holds row
+  // 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32
+  const int n = n0 + wave * 32 + li;
+  if (n >= N) return;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = m0 + 32 * i + 8 * (r >> 2) + 4 * lk + (r & 3);
+      if (m < M) {
+        float* o = Out + (uint64_t)m * ldo + n;
+        *o = ADD ? *o + acc[i][r] : acc[i][r];
+      }
+    }
+}
+
+// The QKV output of token m (packed row order: row pairs are RoPE partners
+// (i, i + hd/2) of a q or k head, or consecutive value dims): rotate q and k
+// at position pos0 + m, write q scaled by log2(e)/sqrt(hd) in natural order
+// to Qn, and k and v rounded to fp16 into the cache -- the decode kernel's
+// QKV epilogue, one token per workgroup.
+__global__ void __launch_bounds__(kRowThreads) rope_kv(float* Qn, const float* Gb, int ldg, uint16_t* kv,
+                                                       const float2* rope, Dims m, int l, int pos0) {
+  const int mq = blockIdx.x, pos = pos0 + mq;
+  const int hd = m.hd, qd = m.H * hd, kvd = m.Hkv * hd;
+  const float qscale = 1.4426950408889634f / sqrtf((float)hd);
+  const float* y = Gb + (uint64_t)mq * ldg;
+  for (int t = threadIdx.x; t < (qd + 2 * kvd) / 2; t += blockDim.x) {
+    const int rr = 2 * t;
+    const float y0 = y[rr], y1 = y[rr + 1];
+    if (rr < qd + kvd) {
+      const bool isq = rr < qd;
+      const int base = isq ? 0 : qd;
+      const int head = (rr - base) / hd;
+      const int i = ((rr - base) % hd) >> 1;
+      const float2 cs = rope[(uint64_t)pos * (hd / 2) + i];
+      const float a = y0 * cs.x - y1 * cs.y;
+      const float b = y0 * cs.y + y1 * cs.x;
+      if (isq) {
+        float* q = Qn + (uint64_t)mq * qd + (uint64_t)head * hd;
+        q[i] = a * qscale;
+        q[i + hd / 2] = b * qscale;
+      } else {
+        uint16_t* kc = kv + kv_offset(m, l, 0, head) + (uint64_t)pos * hd;
+        kc[i] = __half_as_ushort(__float2half_rn(a));
+        kc[i + hd / 2] = __half_as_ushort(__float2half_rn(b));
+      }
+    } else {
+      const int jv = rr - qd - kvd;
+      const int head = jv / hd, dd = jv % hd;
+      uint16_t* vc = kv + kv_offset(m, l, 1, head) + (uint64_t)pos * hd;
+      vc[dd] = __half_as_ushort(__float2half_rn(y0));
+      vc[dd + 1] = __half_as_ushort(__float2half_rn(y1));
+    }
+  }
+}
+
+// Causal attention of the chunk's queries over the cache: one wave per
+// (query token, query head).  Keys go 64 at a time, one per lane (its score
+// is the lane's own dot product); an online softmax in the log2 domain
+// rescales the running sums once per block; each lane accumulates the output
+// dims lane, lane + 64, ... (at most kMaxDims of them).
+constexpr int kMaxDims = 8;  // hd <= 512
+
+__global__ void __launch_bounds__(256) attention(float* Ao, const float* Qn, const uint16_t* kv, Dims m, int l,
+                                                 int pos0, int C) {
+  extern __shared__ float qsh[];  // [4][hd]
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int gw = blockIdx.x * 4 + wave;
+  const int hd = m.hd, H = m.H, qd = H * hd;
+  const int mq = gw / H, h = gw % H;
+  float* q = qsh + wave * hd;
+  if (mq < C) {
+    for (int i = lane; i < hd; i += 64) q[i] = Qn[(uint64_t)mq * qd + (uint64_t)h * hd + i];
+  }
+  __syncthreads();
+  if (mq >= C) return;
+  const int g = h / m.G;
+  const int nkeys = pos0 + mq + 1;
+  const uint16_t* K = kv + kv_offset(m, l, 0, g);
+  const uint16_t* V = kv + kv_offset(m, l, 1, g);
+  float acc[kMaxDims];
+#pragma unroll
+  for (int e = 0; e < kMaxDims; ++e) acc[e] = 0.f;
+  float mrun = -INFINITY, lrun = 0.f;
+  for (int j0 = 0; j0 < nkeys; j0 += 64) {
+    const int j = j0 + lane;
+    float s = -INFINITY;
+    if (j < nkeys) {
+      const uint16_t* kr = K + (uint64_t)j * hd;
+      float t = 0.f;
+      for (int d0 = 0; d0 < hd; d0 += 8) {
+        const uint4 w = *(const uint4*)(kr + d0);
+        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          t = __builtin_fmaf(h2f((uint16_t)(ww[e] & 0xFFFF)), q[d0 + 2 * e], t);
+          t = __builtin_fmaf(h2f((uint16_t)(ww[e] >> 16)), q[d0 + 2 * e + 1], t);
+        }
+      }
+      s = t;
+    }
+    float bm = s;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) bm = fmaxf(bm, __shfl_xor(bm, off));
+    const float mn = fmaxf(mrun, bm);
+    const float scale = mrun == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mrun - mn);
+    const float p = s == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(s - mn);
+    float ps = p;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) ps += __shfl_xor(ps, off);
+    lrun = lrun * scale + ps;
+    mrun = mn;
+#pragma unroll
+    for (int e = 0; e < kMaxDims; ++e) acc[e] *= scale;
+    const int nb = nkeys - j0 < 64 ? nkeys - j0 : 64;
+    for (int jj = 0; jj < nb; ++jj) {
+      const float pj = __shfl(p, jj);
+      const uint16_t* vr = V + (uint64_t)(j0 + jj) * hd;
+#pragma unroll
+      for (int e = 0; e < kMaxDims; ++e) {
+        const int dd = lane + 64 * e;
+        if (dd < hd) acc[e] = __builtin_fmaf(pj, h2f(vr[dd]), acc[e]);
+      }
+    }
+  }
+  float* o = Ao + (uint64_t)mq * qd + (uint64_t)h * hd;
+#pragma unroll
+  for (int e = 0; e < kMaxDims; ++e) {
+    const int dd = lane + 64 * e;
+    if (dd < hd) o[dd] = acc[e] / lrun;
+  }
+}
+
+// Y[m][j] = silu(G[m][2j]) * G[m][2j+1] (gate/up rows interleaved)
+__global__ void __launch_bounds__(kRowThreads) swiglu(float* Y, int ldy, const float* Gb, int ldg, int F) {
+  const int m = blockIdx.x;
+  const float* g = Gb + (uint64_t)m * ldg;
+  for (int j = threadIdx.x; j < F; j += blockDim.x) {
+    const float y0 = g[2 * j], y1 = g[2 * j + 1];
+    Y[(uint64_t)m * ldy + j] = y0 / (1.0f + expf(-y0)) * y1;
+  }
+}
+
+}  // namespace pf
+}  // namespace kie
+
+using namespace kie;
+
+static hipError_t launch_gemm(bool add, float* Out, int ldo, const float* A, int lda, const uint16_t* Wm, int M, int N,
+                              int K, hipStream_t st) {
+  const dim3 grid((N + pf::BN - 1) / pf::BN, (M + pf::BM - 1) / pf::BM);
+  if (add) {
+    hipLaunchKernelGGL(pf::gemm<true>, grid, dim3(256), 0, st, Out, ldo, A, lda, Wm, M, N, K);
+  } else {
+    hipLaunchKernelGGL(pf::gemm<false>, grid, dim3(256), 0, st, Out, ldo, A, lda, Wm, M, N, K);
+  }
+  return hipGetLastError();
+}
+
+// every layer of one chunk of prompt tokens; asynchronous on `st`
+extern "C" hipError_t kie_internal_prefill_chunk(const PrefillArgs* a, hipStream_t st) {
+  const Dims& m = a->m;
+  const int C = a->C;
+  if (C <= 0) return hipSuccess;
+  if (m.parallel || m.hd > 64 * pf::kMaxDims || (m.hd & 7)) return hipErrorInvalidValue;
+  const int d = m.d, qd = m.H * m.hd, kvd = m.Hkv * m.hd, F = m.F;
+  const int ly = pf_ycols(m), lg = pf_gcols(m);
+  float* X = a->scratch;
+  float* Y = X + (uint64_t)C * d;
+  float* Gb = Y + (uint64_t)C * ly;
+  float* Qn = Gb + (uint64_t)C * lg;
+  float* Ao = Qn + (uint64_t)C * qd;
+  hipError_t e;
+  hipLaunchKernelGGL(pf::embed, dim3(C), dim3(pf::kRowThreads), 0, st, X, a->W, a->pl.embed, a->tokens, d, m.V,
+                     a->state);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int attn_blocks = (C * m.H + 3) / 4;
+  const size_t attn_lds = (size_t)4 * m.hd * sizeof(float);
+  for (int l = 0; l < m.L; ++l) {
+    const uint16_t* Wl = a->W + (uint64_t)l * a->pl.layer_stride;
+    hipLaunchKernelGGL(pf::rmsnorm, dim3(C), dim3(pf::kRowThreads), 0, st, Y, ly, X, d, Wl + a->pl.attn_norm, m.eps);
+    if ((e = launch_gemm(false, Gb, lg, Y, ly, Wl + a->pl.wqkv, C, qd + 2 * kvd, d, st)) != hipSuccess) return e;
+    hipLaunchKernelGGL(pf::rope_kv, dim3(C), dim3(pf::kRowThreads), 0, st, Qn, Gb, lg, a->kv, a->rope, m, l, a->pos0);
+    hipLaunchKernelGGL(pf::attention, dim3(attn_blocks), dim3(256), attn_lds, st, Ao, Qn, a->kv, m, l, a->pos0, C);
+    if ((e = launch_gemm(true, X, d, Ao, qd, Wl + a->pl.wo, C, d, qd, st)) != hipSuccess) return e;
+    hipLaunchKernelGGL(pf::rmsnorm, dim3(C), dim3(pf::kRowThreads), 0, st, Y, ly, X, d, Wl + a->pl.mlp_norm, m.eps);
+    if ((e = launch_gemm(false, Gb, lg, Y, ly, Wl + a->pl.wgu, C, 2 * F, d, st)) != hipSuccess) return e;
+    hipLaunchKernelGGL(pf::swiglu, dim3(C), dim3(pf::kRowThreads), 0, st, Y, ly, Gb, lg, F);
+    if ((e = launch_gemm(true, X, d, Y, ly, Wl + a->pl.wd, C, d, F, st)) != hipSuccess) return e;
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}

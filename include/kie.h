@@ -132,6 +132,29 @@ kie_status kie_load_weights(kie_ctx* ctx, const kie_weights* host_src, void* str
 kie_status kie_prefill(kie_ctx* ctx, const int32_t* d_prompt, int32_t n_prompt, int32_t* d_next_token,
                        float* d_logits, void* stream);
 
+/* Bytes of device scratch kie_prefill_batched needs to process chunk_tokens
+ * prompt tokens per chunk (fp32 activations of the chunk). */
+kie_status kie_prefill_scratch_bytes(const kie_ctx* ctx, int32_t chunk_tokens, size_t* bytes);
+
+/* kie_prefill with the prompt batched: the same result (KV cache rows for
+ * positions pos..pos+n_prompt-1, t1, the last position's logits, position
+ * += n_prompt), computed as dense products on the matrix cores.  The pages'
+ * monokernel runs prefill on the GPU (Kog explainer, "Monokernel" section);
+ * batching the prompt reads every weight once per chunk of tokens instead
+ * of once per token.  All prompt tokens but the last go through batched
+ * GEMMs (fp32 activations, fp16 weights, fp32 accumulation), RoPE, fp16 KV
+ * append and causal attention, chunk by chunk; the last one runs through
+ * the decode kernel, which yields t1 (greedy or sampled, see
+ * kie_set_sampling).  d_scratch is caller-owned device memory (16-byte
+ * aligned) of scratch_bytes; the chunk is the largest that fits, at most
+ * 1024 tokens (kie_prefill_scratch_bytes gives the size for a chunk).  The
+ * lane-structured block (n_lanes > 1), ffn_dim not a multiple of 4 and a
+ * one-token prompt fall back to kie_prefill.  KIE_ERR_INVALID_ARG if the
+ * scratch cannot hold one token; an out-of-range id latches
+ * KIE_ERR_BAD_TOKEN as in kie_prefill.  Asynchronous on `stream`. */
+kie_status kie_prefill_batched(kie_ctx* ctx, const int32_t* d_prompt, int32_t n_prompt, int32_t* d_next_token,
+                               float* d_logits, void* d_scratch, size_t scratch_bytes, void* stream);
+
 /* Run n_tokens decode steps.  Step k consumes d_forced_in[k] when that
  * pointer is not NULL (teacher forcing), else the previous step's argmax (the
  * pending token for k = 0); it runs at position pos + k, writes its greedy
