@@ -103,16 +103,29 @@ def _rows(d, suffix):
 
 
 def summarize_trace(d: str, command: str) -> str:
-    """markdown: per-kernel stats and every monokernel dispatch"""
+    """markdown: per-kernel stats and every monokernel dispatch (for a trace of
+    the --prefill mode: per-kernel stats and the batched prefill's share)"""
     stats = _rows(d, "kernel_stats.csv")
     trace = _rows(d, "kernel_trace.csv")
-    out = ["# rocprofv3 kernel trace of the default benchmark run (cfg2, 2048-token prompt, 512 decode steps)", "",
-           "Command (from the repository root on the GPU box):", "", "```", command, "```", "",
+    prefill = "--prefill" in command
+    title = ("# rocprofv3 kernel trace of the batched prefill benchmark (cfg2, 2048-token prompt, chunks of 1024)"
+             if prefill else
+             "# rocprofv3 kernel trace of the default benchmark run (cfg2, 2048-token prompt, 512 decode steps)")
+    out = [title, "", "Command (from the repository root on the GPU box):", "", "```", command, "```", "",
            "| kernel | calls | total ms | average ms | min ms | max ms |", "|---|---|---|---|---|---|"]
     for r in stats:
         ns = lambda k: float(r[k]) / 1e6
         out.append(f"| `{r['Name'][:70]}` | {r['Calls']} | {ns('TotalDurationNs'):.3f} | {ns('AverageNs'):.3f} | "
                    f"{ns('MinNs'):.3f} | {ns('MaxNs'):.3f} |")
+    if prefill:
+        tot = sum(float(r["TotalDurationNs"]) for r in stats if "kie::" in r["Name"])
+        out += ["", "Share of the kie kernels' time (two prefills: a warm-up and the timed one; in each, all "
+                "prompt tokens but the last run through the batched kernels, the last through one decode-kernel "
+                "launch):", "", "| kernel | share |", "|---|---|"]
+        for r in stats:
+            if "kie::" in r["Name"]:
+                out.append(f"| `{r['Name'][:70]}` | {100 * float(r['TotalDurationNs']) / tot:.1f} % |")
+        return "\n".join(out) + "\n"
     mk = [r for r in trace if "kie_monokernel" in r["Kernel_Name"]]
     out += ["", "Every launch of the persistent kernel, in order: the prompt's launches, the warm-up decode, "
             "then the timed decode (the last row; bench.py's HIP events time the same launch).", "",
@@ -174,6 +187,9 @@ def main():
                     help="print the JSON traffic summary of two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) "
                          "of this command with --copy-bytes and exit")
     ap.add_argument("--command", default="", help="the profiled command, recorded in a summary")
+    ap.add_argument("--prefill", action="store_true",
+                    help="instead of the decode benchmark, time the batched prefill of the prompt and print "
+                         "its own JSON line (matrix-core roofline)")
     args = ap.parse_args()
 
     if args.summarize_trace:
@@ -208,7 +224,10 @@ def main():
     eng = Engine(cfg, device=0, max_ctx=max_ctx)
     eng.set_launch_steps(max(K, W, 1))
     eng.load_weights(w)
-    t1 = eng.prefill(prompt)
+    if args.prefill:
+        prefill_bench(args, cfg, eng, prompt)
+        return
+    t1 = eng.prefill_batched(prompt)
     dev = eng.dev
     out = torch.empty(max(K, W), dtype=torch.int32, device=dev)
     print(f"bench: {cfg.name} setup {time.time() - t_setup:.1f}s (P={P}, t1={t1})", file=sys.stderr, flush=True)
@@ -297,6 +316,65 @@ def main():
         del src, dst
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, w, P, args.cpu_steps)
+    print(json.dumps(res), flush=True)
+
+
+PEAK_FP32_MFMA_TFLOPS = 157.3  # MI355X dense fp32 matrix rate
+
+
+def prefill_flops(cfg, n_tokens: int) -> float:
+    """GEMM and attention FLOPs of pushing prompt tokens 0..n_tokens-1 through
+    the layers (2 per multiply-add)"""
+    d, hd, H, Hkv, F, L = cfg.d_model, cfg.head_dim, cfg.n_heads, cfg.n_kv_heads, cfg.ffn_dim, cfg.n_layers
+    per_token_params = (H + 2 * Hkv) * hd * d + d * H * hd + 2 * F * d + d * F
+    gemm = 2.0 * per_token_params * L * n_tokens
+    attn = 4.0 * hd * H * L * (n_tokens * (n_tokens + 1) / 2)  # q.k and p.v over keys 0..i
+    return gemm + attn
+
+
+def prefill_bench(args, cfg, eng, prompt):
+    """time kie_prefill_batched over the whole prompt (the batched part covers
+    all tokens but the last, which runs through the decode kernel)"""
+    import torch
+    P = len(prompt)
+    dev = eng.dev
+    d_prompt = torch.tensor(np.asarray(prompt, dtype=np.int32), device=dev)
+    d_next = torch.empty(1, dtype=torch.int32, device=dev)
+    chunk = 1024
+    scratch = torch.empty(eng.prefill_scratch_bytes(chunk) // 4, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    times = []
+    for it in range(1 + max(1, args.repeats)):
+        eng.set_position(0, 0)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        eng.prefill_batched_device(d_prompt, P, d_next, scratch)
+        b.record(stream)
+        torch.cuda.synchronize()
+        eng.sync()
+        if it > 0:  # the first run is a warm-up
+            times.append(a.elapsed_time(b))
+    ms = float(np.median(times))
+    flops = prefill_flops(cfg, P - 1)
+    achieved = flops / (ms * 1e-3) / 1e12
+    res = {
+        "metric": "batched prefill tokens/s on 1 MI355X + achieved fp32 matrix TFLOP/s vs peak",
+        "value": round(P / (ms * 1e-3), 1),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "ms": round(ms, 3),
+        "higher_is_better": True,
+        "dtype": "fp32 (fp16 weights)",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: {cfg.description}; batched prefill of a {P}-token prompt, "
+                               f"chunks of {chunk}", "prompt_len": P},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_FP32_MFMA_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_MFMA_TFLOPS, 4), "traffic": None,
+                     "flops": flops, "all_ms": [round(x, 3) for x in times]},
+        "next_token": int(d_next.cpu()[0]),
+    }
+    eng.close()
     print(json.dumps(res), flush=True)
 
 

@@ -288,6 +288,19 @@ class Engine:
             return tok, d_logits.cpu().numpy()
         return tok
 
+    def prefill_scratch_bytes(self, chunk: int) -> int:
+        nbytes = C.c_size_t()
+        _check(self.L.kie_prefill_scratch_bytes(self.ctx, int(chunk), C.byref(nbytes)), self.ctx)
+        return int(nbytes.value)
+
+    def prefill_batched_device(self, d_prompt, n: int, d_next, scratch, d_logits=None):
+        """asynchronous kie_prefill_batched on caller-provided device tensors"""
+        _check(self.L.kie_prefill_batched(self.ctx, d_prompt.data_ptr(), int(n),
+                                          d_next.data_ptr() if d_next is not None else None,
+                                          d_logits.data_ptr() if d_logits is not None else None,
+                                          scratch.data_ptr(), scratch.numel() * scratch.element_size(),
+                                          self.stream()), self.ctx)
+
     def prefill_batched(self, prompt: Sequence[int], want_logits: bool = False, chunk: int = 1024):
         """kie_prefill_batched with a scratch buffer for `chunk` tokens"""
         t = self.torch
