@@ -294,6 +294,163 @@ __global__ void __launch_bounds__(256) attention(float* Ao, const float* Qn, con
   }
 }
 
+// Causal attention on the matrix cores (flash-attention order): a workgroup
+// takes 64 query tokens of one head, wave w the 16 tokens 16w .. 16w+15.  Key
+// blocks of 64 are staged in LDS as fp32 (K and V of the head's KV head,
+// zero past the last key) and shared by the four waves.  Per block, with
+// v_mfma_f32_16x16x4f32: S = Q K^T (16 x 64 per wave, the log2-domain scores),
+// masked above the diagonal; a row-wise online softmax (max and sum over the
+// 16 lanes holding a row's columns, DPP); P goes through LDS into the A-operand
+// layout; O += P V.  fp32 throughout, like the decode kernel's attention.
+// For hd a multiple of 16 and at most 128 (larger heads use `attention`).
+typedef float f4v __attribute__((ext_vector_type(4)));
+constexpr int FQ = 64, FK = 64;  // query tokens and keys per block
+
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false)));
+  return v;
+}
+__device__ __forceinline__ float row16_add(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
+  return v;
+}
+
+template <int HD>
+__global__ void __launch_bounds__(256) attention_mfma(float* Ao, const float* Qn, const uint16_t* kv, Dims m, int l,
+                                                      int pos0, int C) {
+  constexpr int KS = HD + 4;   // K row stride (floats): conflict-free B-operand reads
+  constexpr int VS = HD + 16;  // V row stride
+  constexpr int PS = FK + 4;   // P row stride
+  constexpr int NS = HD / 4;   // k-steps of Q K^T
+  constexpr int NU = HD / 16;  // 16-wide output column tiles
+  __shared__ float Ks[FK * KS];
+  __shared__ float Vs[FK * VS];
+  __shared__ float Ps[4][16 * PS];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int lr = lane & 15, lq = lane >> 4;
+  const int qb = blockIdx.x, h = blockIdx.y;
+  const int H = m.H, qd = H * HD, g = h / m.G;
+  const int t0 = qb * FQ + wave * 16;  // this wave's first token in the chunk
+  // Q fragments: lane holds Q[token t0 + lr][dim 4s + lq] for s < NS
+  float qf[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const int t = t0 + lr;
+    qf[s] = t < C ? Qn[(uint64_t)t * qd + (uint64_t)h * HD + 4 * s + lq] : 0.f;
+  }
+  f4v acc[NU];
+#pragma unroll
+  for (int u = 0; u < NU; ++u) acc[u] = f4v{0.f, 0.f, 0.f, 0.f};
+  float mrow[4], lrow[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    mrow[r] = -INFINITY;
+    lrow[r] = 0.f;
+  }
+  // query positions of the rows this lane holds in the S and O layouts
+  int qpos[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) qpos[r] = pos0 + t0 + 4 * lq + r;
+  const int last_tok = min(C, qb * FQ + FQ) - 1;
+  const int nkeys = pos0 + last_tok + 1;  // keys the block's last query sees
+  const uint16_t* K = kv + kv_offset(m, l, 0, g);
+  const uint16_t* V = kv + kv_offset(m, l, 1, g);
+  float* P = Ps[wave];
+  for (int k0 = 0; k0 < nkeys; k0 += FK) {
+    __syncthreads();  // the previous block's K, V are consumed
+    // stage keys k0 .. k0+63: 8 halves per thread and pass
+    for (int i = tid; i < FK * HD / 8; i += 256) {
+      const int key = i / (HD / 8), c = (i % (HD / 8)) * 8;
+      uint4 kw = make_uint4(0, 0, 0, 0), vw = make_uint4(0, 0, 0, 0);
+      if (k0 + key < nkeys) {
+        kw = *(const uint4*)(K + (uint64_t)(k0 + key) * HD + c);
+        vw = *(const uint4*)(V + (uint64_t)(k0 + key) * HD + c);
+      }
+      const uint32_t kk[4] = {kw.x, kw.y, kw.z, kw.w}, vv[4] = {vw.x, vw.y, vw.z, vw.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        Ks[key * KS + c + 2 * e] = h2f((uint16_t)(kk[e] & 0xFFFF));
+        Ks[key * KS + c + 2 * e + 1] = h2f((uint16_t)(kk[e] >> 16));
+        Vs[key * VS + c + 2 * e] = h2f((uint16_t)(vv[e] & 0xFFFF));
+        Vs[key * VS + c + 2 * e + 1] = h2f((uint16_t)(vv[e] >> 16));
+      }
+    }
+    __syncthreads();
+    // S = Q K^T for the 4 key tiles of 16
+    f4v sc[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      sc[kt] = f4v{0.f, 0.f, 0.f, 0.f};
+      const float* kr = Ks + (kt * 16 + lr) * KS + lq;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) sc[kt] = __builtin_amdgcn_mfma_f32_16x16x4f32(qf[s], kr[4 * s], sc[kt], 0, 0, 0);
+    }
+    // mask (key position > query position, or past the keys) and row maxima
+    float bm[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      const int kpos = k0 + kt * 16 + lr;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (kpos > qpos[r]) sc[kt][r] = -INFINITY;
+        bm[r] = fmaxf(bm[r], sc[kt][r]);
+      }
+    }
+    float scale[4], mn[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      bm[r] = row16_max(bm[r]);
+      mn[r] = fmaxf(mrow[r], bm[r]);
+      scale[r] = mn[r] == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(mrow[r] - mn[r]);
+    }
+    float rs[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = sc[kt][r] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sc[kt][r] - mn[r]);
+        rs[r] += p;
+        P[(4 * lq + r) * PS + kt * 16 + lr] = p;  // P[row][key]
+      }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      lrow[r] = lrow[r] * scale[r] + row16_add(rs[r]);
+      mrow[r] = mn[r];
+    }
+#pragma unroll
+    for (int u = 0; u < NU; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[u][r] *= scale[r];
+    // the wave's own P tile: its LDS writes must land before its reads
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    __builtin_amdgcn_wave_barrier();
+    // O += P V: A = P[row lr][key 4s + lq], B = V[key 4s + lq][dim 16u + lr]
+#pragma unroll 4
+    for (int s = 0; s < FK / 4; ++s) {
+      const float pa = P[lr * PS + 4 * s + lq];
+      const float* vr = Vs + (4 * s + lq) * VS + lr;
+#pragma unroll
+      for (int u = 0; u < NU; ++u) acc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa, vr[16 * u], acc[u], 0, 0, 0);
+    }
+  }
+  // O = acc / l, rows 4 lq + r, columns 16u + lr
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int t = t0 + 4 * lq + r;
+    if (t >= C) continue;
+    float* o = Ao + (uint64_t)t * qd + (uint64_t)h * HD;
+    const float inv = 1.0f / lrow[r];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) o[16 * u + lr] = acc[u][r] * inv;
+  }
+}
+
 // Y[m][j] = silu(G[m][2j]) * G[m][2j+1] (gate/up rows interleaved)
 __global__ void __launch_bounds__(kRowThreads) swiglu(float* Y, int ldy, const float* Gb, int ldg, int F) {
   const int m = blockIdx.x;
@@ -344,7 +501,16 @@ extern "C" hipError_t kie_internal_prefill_chunk(const PrefillArgs* a, hipStream
     hipLaunchKernelGGL(pf::rmsnorm, dim3(C), dim3(pf::kRowThreads), 0, st, Y, ly, X, d, Wl + a->pl.attn_norm, m.eps);
     if ((e = launch_gemm(false, Gb, lg, Y, ly, Wl + a->pl.wqkv, C, qd + 2 * kvd, d, st)) != hipSuccess) return e;
     hipLaunchKernelGGL(pf::rope_kv, dim3(C), dim3(pf::kRowThreads), 0, st, Qn, Gb, lg, a->kv, a->rope, m, l, a->pos0);
-    hipLaunchKernelGGL(pf::attention, dim3(attn_blocks), dim3(256), attn_lds, st, Ao, Qn, a->kv, m, l, a->pos0, C);
+    const dim3 fa_grid((C + pf::FQ - 1) / pf::FQ, m.H);
+    switch (m.hd) {
+      case 32: hipLaunchKernelGGL(pf::attention_mfma<32>, fa_grid, dim3(256), 0, st, Ao, Qn, a->kv, m, l, a->pos0, C); break;
+      case 64: hipLaunchKernelGGL(pf::attention_mfma<64>, fa_grid, dim3(256), 0, st, Ao, Qn, a->kv, m, l, a->pos0, C); break;
+      case 80: hipLaunchKernelGGL(pf::attention_mfma<80>, fa_grid, dim3(256), 0, st, Ao, Qn, a->kv, m, l, a->pos0, C); break;
+      case 96: hipLaunchKernelGGL(pf::attention_mfma<96>, fa_grid, dim3(256), 0, st, Ao, Qn, a->kv, m, l, a->pos0, C); break;
+      case 128: hipLaunchKernelGGL(pf::attention_mfma<128>, fa_grid, dim3(256), 0, st, Ao, Qn, a->kv, m, l, a->pos0, C); break;
+      default:
+        hipLaunchKernelGGL(pf::attention, dim3(attn_blocks), dim3(256), attn_lds, st, Ao, Qn, a->kv, m, l, a->pos0, C);
+    }
     if ((e = launch_gemm(true, X, d, Ao, qd, Wl + a->pl.wo, C, d, qd, st)) != hipSuccess) return e;
     hipLaunchKernelGGL(pf::rmsnorm, dim3(C), dim3(pf::kRowThreads), 0, st, Y, ly, X, d, Wl + a->pl.mlp_norm, m.eps);
     if ((e = launch_gemm(false, Gb, lg, Y, ly, Wl + a->pl.wgu, C, 2 * F, d, st)) != hipSuccess) return e;
