@@ -8,8 +8,9 @@ prompt in seconds, so the full sizes are covered three ways:
   full width and depth; cfg4's width, GQA and vocabulary with two layers);
 * a long-context GQA model whose every wave walks many key steps, against the
   oracle after a 4096-token prompt;
-* the launch configuration the benchmark times (cfg2, 2048-token prompt, 512
-  decode steps in one launch): layer-0 keys and values at sampled prompt
+* the launch configuration the benchmark times (cfg2, 2048-token prompt
+  through the batched prefill, 512 decode steps in one launch): layer-0 keys
+  and values at sampled prompt
   positions against the oracle (they depend only on the prompt token and
   the position, so they pin the QKV GEMV, RoPE far along the context and the
   KV append at full size), the same for cfg4's RoPE base over a 32768-token
@@ -131,8 +132,9 @@ def assert_kv_close(gpu, ref, name):
 
 
 def test_bench_configuration():
-    """cfg2, 2048-token prompt, 512 decode steps in one launch (what bench.py
-    times): layer-0 KV against the oracle, bitwise repeat, chunked launches"""
+    """cfg2, 2048-token prompt prefilled in batches, 512 decode steps in one
+    launch (what bench.py times): layer-0 KV written by the batched prefill
+    against the oracle, bitwise repeat, chunked launches"""
     cfg = CFG2
     P, N = cfg.prompt_len, cfg.decode_steps
     say(f"case bench configuration {cfg.name}: P={P} N={N}")
@@ -141,7 +143,7 @@ def test_bench_configuration():
     eng = make_engine(cfg, P + N)
     eng.set_launch_steps(N)
     eng.load_weights(w)
-    t1 = eng.prefill(prompt)
+    t1 = eng.prefill_batched(prompt)
     pos = np.unique(np.concatenate([np.arange(0, 8), np.arange(8, P, 97), [P - 2, P - 1]]))
     kref, vref = layer0_kv_reference(cfg, w, prompt, pos)
     assert_kv_close(gpu_kv_rows(eng, cfg, 0, 0, pos), kref, "cfg2 layer-0 K")
