@@ -1151,12 +1151,15 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
               if (mine) online_update(mrow[h], lrow[h], acc[h], t, vx);
             }
           }
-          // merge this wave's key slots into lanes 0..lpk-1.  Only those
-          // lanes accumulate; every other lane keeps its own slot's state, so
-          // each slot is counted exactly once.
-          const bool dst = D.lane < D.lpk;
-          for (int k = 1; k < D.kpl; ++k) {
-            const int src = D.lane + k * D.lpk;
+          // merge this wave's key slots into slot 0 (lanes 0..lpk-1) as a
+          // tree: with span s, slot j < s takes in slot j + s (when it
+          // exists), for s = the largest power of two below kpl, then halves.
+          // Every slot is counted exactly once.
+          int span = 1;
+          while (span * 2 < D.kpl) span *= 2;
+          for (; span >= 1; span >>= 1) {
+            const int src = (D.lane + span * D.lpk) & (kWave - 1);
+            const bool take = D.kl < span && D.kl + span < D.kpl;
 #pragma unroll
             for (int h = 0; h < G; ++h) {
               const float mo = __shfl(mrow[h], src);
@@ -1164,7 +1167,7 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
               float ao[8];
 #pragma unroll
               for (int e = 0; e < 8; ++e) ao[e] = __shfl(acc[h][e], src);
-              if (dst) lse_merge(mrow[h], lrow[h], acc[h], mo, lo, ao);
+              if (take) lse_merge(mrow[h], lrow[h], acc[h], mo, lo, ao);
             }
           }
           if (D.lane < D.lpk) {
