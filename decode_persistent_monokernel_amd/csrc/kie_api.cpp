@@ -373,9 +373,9 @@ kie_status kie_prefill_batched(kie_ctx* c, const int32_t* d_prompt, int32_t n, i
   if (s != KIE_OK) return s;
   if (!d_prompt || n <= 0) return fail(c, KIE_ERR_INVALID_ARG, "empty prompt");
   if ((int64_t)c->pos + n > c->m.max_ctx) return fail(c, KIE_ERR_CAPACITY, "prompt exceeds max_ctx");
-  // the lane-structured block, and shapes the batched kernels do not take,
-  // run token by token; so does a one-token prompt
-  const bool batched = !c->m.parallel && n > 1 && c->m.hd <= 512 && (c->m.hd % 8) == 0 && (c->m.F % 4) == 0;
+  // shapes the batched kernels do not take run token by token; so does a
+  // one-token prompt
+  const bool batched = n > 1 && c->m.hd <= 512 && (c->m.hd % 8) == 0 && (c->m.F % 4) == 0;
   if (!batched) return kie_prefill(c, d_prompt, n, d_next, d_logits, stream);
   if (!d_scratch || ((uintptr_t)d_scratch & 15))
     return fail(c, KIE_ERR_INVALID_ARG, "prefill scratch must be a 16-byte aligned device buffer");

@@ -381,6 +381,8 @@ constexpr int kTracePhases = 5 * 64 + 2;  // up to 64 layers, LM, step end
 //   Gb [C][max(qd+2kvd, 2F)] QKV or gate/up GEMM output (packed row order)
 //   Qn [C][qd]               rotated queries, scaled by log2(e)/sqrt(hd)
 //   Ao [C][qd]               attention output (natural head-major order)
+// and for the lane-structured block P [C][d] and R [delay + 2][C][d]
+// (X then holds x_0, the embedding).
 struct PrefillArgs {
   Dims m;
   PackLayout pl;
@@ -397,9 +399,12 @@ KIE_HD int pf_gcols(const Dims& m) {
   const int qkv = (m.H + 2 * m.Hkv) * m.hd;
   return qkv > 2 * m.F ? qkv : 2 * m.F;
 }
-// fp32 scratch floats per prompt token of a chunk
+// fp32 scratch floats per prompt token of a chunk; the lane-structured
+// block adds its partial sums P [C][d] and delay + 2 residual states
+// R_l = x_0 + P_0 + .. + P_l [C][d] (layer l reads R_{l - delay - 1})
 KIE_HD uint64_t pf_floats_per_token(const Dims& m) {
-  return (uint64_t)m.d + pf_ycols(m) + pf_gcols(m) + 2ull * m.H * m.hd;
+  return (uint64_t)m.d + pf_ycols(m) + pf_gcols(m) + 2ull * m.H * m.hd +
+         (m.parallel ? (uint64_t)(m.delay + 3) * m.d : 0ull);
 }
 
 enum DebugFlags : uint32_t {

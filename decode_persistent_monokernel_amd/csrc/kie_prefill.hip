@@ -461,6 +461,12 @@ __global__ void __launch_bounds__(kRowThreads) swiglu(float* Y, int ldy, const f
   }
 }
 
+// R = A + B elementwise (the lane block's residual update R_l = R_{l-1} + P_l)
+__global__ void __launch_bounds__(256) radd(float* R, const float* A, const float* B, uint64_t n) {
+  for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (uint64_t)gridDim.x * blockDim.x)
+    R[i] = A[i] + B[i];
+}
+
 }  // namespace pf
 }  // namespace kie
 
@@ -478,44 +484,70 @@ static hipError_t launch_gemm(bool add, float* Out, int ldo, const float* A, int
 }
 
 // every layer of one chunk of prompt tokens; asynchronous on `st`
+static void launch_attention(const Dims& m, int l, float* Ao, const float* Qn, uint16_t* kv, int pos0, int C,
+                             hipStream_t st) {
+  const dim3 fa_grid((C + pf::FQ - 1) / pf::FQ, m.H);
+  switch (m.hd) {
+    case 32: hipLaunchKernelGGL(pf::attention_mfma<32>, fa_grid, dim3(256), 0, st, Ao, Qn, kv, m, l, pos0, C); break;
+    case 64: hipLaunchKernelGGL(pf::attention_mfma<64>, fa_grid, dim3(256), 0, st, Ao, Qn, kv, m, l, pos0, C); break;
+    case 80: hipLaunchKernelGGL(pf::attention_mfma<80>, fa_grid, dim3(256), 0, st, Ao, Qn, kv, m, l, pos0, C); break;
+    case 96: hipLaunchKernelGGL(pf::attention_mfma<96>, fa_grid, dim3(256), 0, st, Ao, Qn, kv, m, l, pos0, C); break;
+    case 128: hipLaunchKernelGGL(pf::attention_mfma<128>, fa_grid, dim3(256), 0, st, Ao, Qn, kv, m, l, pos0, C); break;
+    default:
+      hipLaunchKernelGGL(pf::attention, dim3((C * m.H + 3) / 4), dim3(256), (size_t)4 * m.hd * sizeof(float), st, Ao,
+                         Qn, kv, m, l, pos0, C);
+  }
+}
+
+// every layer of one chunk of prompt tokens; asynchronous on `st`.
+// Sequential block: x_{l+1} = x_l + attn + mlp, both added into X.  Lane
+// block (parallel, delay d): attn_l and mlp_l both read x_l, their sum P_l
+// joins the residual d layers later, x_l = R_{l-d-1} with R_l = R_{l-1} + P_l
+// and R_j = x_0 for j < 0 (the decode kernel's order of additions).
 extern "C" hipError_t kie_internal_prefill_chunk(const PrefillArgs* a, hipStream_t st) {
   const Dims& m = a->m;
   const int C = a->C;
   if (C <= 0) return hipSuccess;
-  if (m.parallel || m.hd > 64 * pf::kMaxDims || (m.hd & 7)) return hipErrorInvalidValue;
+  if (m.hd > 64 * pf::kMaxDims || (m.hd & 7)) return hipErrorInvalidValue;
   const int d = m.d, qd = m.H * m.hd, kvd = m.Hkv * m.hd, F = m.F;
   const int ly = pf_ycols(m), lg = pf_gcols(m);
+  const uint64_t Cd = (uint64_t)C * d;
   float* X = a->scratch;
-  float* Y = X + (uint64_t)C * d;
+  float* Y = X + Cd;
   float* Gb = Y + (uint64_t)C * ly;
   float* Qn = Gb + (uint64_t)C * lg;
   float* Ao = Qn + (uint64_t)C * qd;
+  float* Pp = Ao + (uint64_t)C * qd;  // lane block: P [C][d], then R [delay + 2][C][d]
+  float* R = Pp + Cd;
+  const int nslot = m.delay + 2;
+  auto Rslot = [&](int j) -> float* { return j < 0 ? X : R + (uint64_t)(j % nslot) * Cd; };
   hipError_t e;
   hipLaunchKernelGGL(pf::embed, dim3(C), dim3(pf::kRowThreads), 0, st, X, a->W, a->pl.embed, a->tokens, d, m.V,
                      a->state);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const int attn_blocks = (C * m.H + 3) / 4;
-  const size_t attn_lds = (size_t)4 * m.hd * sizeof(float);
   for (int l = 0; l < m.L; ++l) {
     const uint16_t* Wl = a->W + (uint64_t)l * a->pl.layer_stride;
-    hipLaunchKernelGGL(pf::rmsnorm, dim3(C), dim3(pf::kRowThreads), 0, st, Y, ly, X, d, Wl + a->pl.attn_norm, m.eps);
+    const float* xin = m.parallel ? Rslot(l - m.delay - 1) : X;
+    hipLaunchKernelGGL(pf::rmsnorm, dim3(C), dim3(pf::kRowThreads), 0, st, Y, ly, xin, d, Wl + a->pl.attn_norm, m.eps);
     if ((e = launch_gemm(false, Gb, lg, Y, ly, Wl + a->pl.wqkv, C, qd + 2 * kvd, d, st)) != hipSuccess) return e;
     hipLaunchKernelGGL(pf::rope_kv, dim3(C), dim3(pf::kRowThreads), 0, st, Qn, Gb, lg, a->kv, a->rope, m, l, a->pos0);
-    const dim3 fa_grid((C + pf::FQ - 1) / pf::FQ, m.H);
-    switch (m.hd) {
-      case 32: hipLaunchKernelGGL(pf::attention_mfma<32>, fa_grid, dim3(256), 0, st, Ao, Qn, a->kv, m, l, a->pos0, C); break;
-      case 64: hipLaunchKernelGGL(pf::attention_mfma<64>, fa_grid, dim3(256), 0, st, Ao, Qn, a->kv, m, l, a->pos0, C); break;
-      case 80: hipLaunchKernelGGL(pf::attention_mfma<80>, fa_grid, dim3(256), 0, st, Ao, Qn, a->kv, m, l, a->pos0, C); break;
-      case 96: hipLaunchKernelGGL(pf::attention_mfma<96>, fa_grid, dim3(256), 0, st, Ao, Qn, a->kv, m, l, a->pos0, C); break;
-      case 128: hipLaunchKernelGGL(pf::attention_mfma<128>, fa_grid, dim3(256), 0, st, Ao, Qn, a->kv, m, l, a->pos0, C); break;
-      default:
-        hipLaunchKernelGGL(pf::attention, dim3(attn_blocks), dim3(256), attn_lds, st, Ao, Qn, a->kv, m, l, a->pos0, C);
+    launch_attention(m, l, Ao, Qn, a->kv, a->pos0, C, st);
+    if (m.parallel) {
+      // P = attn; P += mlp; R_l = R_{l-1} + P
+      if ((e = launch_gemm(false, Pp, d, Ao, qd, Wl + a->pl.wo, C, d, qd, st)) != hipSuccess) return e;
+    } else {
+      if ((e = launch_gemm(true, X, d, Ao, qd, Wl + a->pl.wo, C, d, qd, st)) != hipSuccess) return e;
     }
-    if ((e = launch_gemm(true, X, d, Ao, qd, Wl + a->pl.wo, C, d, qd, st)) != hipSuccess) return e;
-    hipLaunchKernelGGL(pf::rmsnorm, dim3(C), dim3(pf::kRowThreads), 0, st, Y, ly, X, d, Wl + a->pl.mlp_norm, m.eps);
+    hipLaunchKernelGGL(pf::rmsnorm, dim3(C), dim3(pf::kRowThreads), 0, st, Y, ly, xin, d, Wl + a->pl.mlp_norm, m.eps);
     if ((e = launch_gemm(false, Gb, lg, Y, ly, Wl + a->pl.wgu, C, 2 * F, d, st)) != hipSuccess) return e;
     hipLaunchKernelGGL(pf::swiglu, dim3(C), dim3(pf::kRowThreads), 0, st, Y, ly, Gb, lg, F);
-    if ((e = launch_gemm(true, X, d, Y, ly, Wl + a->pl.wd, C, d, F, st)) != hipSuccess) return e;
+    if (m.parallel) {
+      if ((e = launch_gemm(true, Pp, d, Y, ly, Wl + a->pl.wd, C, d, F, st)) != hipSuccess) return e;
+      const int blocks = (int)((Cd + 255) / 256 < 4096 ? (Cd + 255) / 256 : 4096);
+      hipLaunchKernelGGL(pf::radd, dim3(blocks), dim3(256), 0, st, Rslot(l), Rslot(l - 1), Pp, Cd);
+    } else {
+      if ((e = launch_gemm(true, X, d, Y, ly, Wl + a->pl.wd, C, d, F, st)) != hipSuccess) return e;
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;

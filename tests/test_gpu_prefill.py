@@ -84,21 +84,13 @@ def test_small_shapes_batched_prefill(shape):
     check_against_oracle(cfg, w, gen_prompt(cfg), 100, cfg.decode_steps, kv_fp16=True)
 
 
-def test_lane_block_falls_back_to_token_by_token():
+@pytest.mark.parametrize("chunk", [4, 64])
+def test_lane_block_batched_prefill(chunk):
+    # the parallel block with its residual delayed by 2 layers (5 layers, 2 lanes)
     cfg = CFG0.with_(name="lanes", n_layers=5, n_lanes=2, lane_delay=2, sequential=False, seed_index=33,
-                     prompt_len=12, decode_steps=4)
-    say("case batched prefill on the lane block (token-by-token fallback)")
-    w = gen_weights(cfg)
-    prompt = gen_prompt(cfg)
-    a = make_engine(cfg, 16)
-    a.load_weights(w)
-    ta, la = a.prefill_batched(prompt, want_logits=True, chunk=4)
-    b = make_engine(cfg, 16)
-    b.load_weights(w)
-    tb, lb = b.prefill(prompt, want_logits=True)
-    assert ta == tb and np.array_equal(la, lb)
-    a.close()
-    b.close()
+                     prompt_len=40, decode_steps=6)
+    say(f"case batched prefill on the lane block, delay 2, chunk={chunk}")
+    check_against_oracle(cfg, gen_weights(cfg), gen_prompt(cfg), chunk, cfg.decode_steps, kv_fp16=False)
 
 
 def test_bad_token_in_batched_part_is_reported():
