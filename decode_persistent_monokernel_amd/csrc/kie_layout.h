@@ -210,11 +210,27 @@ KIE_HD GemvShape gemv_shape(const Dims& m, int kind) {
 KIE_HD int blocks_per_row(int K) { return (K + kBlock - 1) / kBlock; }
 KIE_HD int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
-// rows [r0, r1) of op `kind` owned by workgroup wg
+// rows [r0, r1) of op `kind` owned by workgroup wg.  The O projection
+// leaves out the attention mergers (the last workgroup of each KV head's
+// group, see attn_segments): they combine their head's partial results after
+// every other workgroup is done with attention, and the O projection's
+// output waits for its slowest producer.  (The parallel block keeps the O
+// rows with the down projection's: a workgroup adds the two outputs of its
+// rows locally.)
 KIE_HD void gemv_rows(const Dims& m, int kind, int nwg, int wg, int* r0, int* r1) {
   GemvShape s = gemv_shape(m, kind);
   int a, b;
-  split(s.rows / s.unit_rows, nwg, wg, &a, &b);
+  if (kind == PH_O && !m.parallel && nwg > m.Hkv) {
+    const int g = split_owner(wg, nwg, m.Hkv);  // the workgroup's KV head group
+    int w0, w1;
+    split(nwg, m.Hkv, g, &w0, &w1);
+    // wg - g: the workgroup's index among the non-mergers (each earlier group
+    // has one merger); a merger gets the empty range where the next one starts
+    split(s.rows / s.unit_rows, nwg - m.Hkv, wg - g, &a, &b);
+    if (wg == w1 - 1) b = a;
+  } else {
+    split(s.rows / s.unit_rows, nwg, wg, &a, &b);
+  }
   *r0 = a * s.unit_rows;
   *r1 = b * s.unit_rows;
 }
