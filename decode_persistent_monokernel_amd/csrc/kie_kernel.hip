@@ -816,6 +816,37 @@ KIE_DI void attn_step(const Dev& D, const u4v kx, const u4v vx, int key, int kc,
   }
 }
 
+// Two key steps whose keys all lie below kc (wave-uniform: the caller
+// checks), folded into each query head's online softmax with one rescale:
+// m' = max(m, s0, s1), acc' = acc 2^(m - m') + p0 v0 + p1 v1 with
+// p = 2^(s - m').  Every score is finite, so 2^(m - m') needs no guard
+// (it is 0 while m is still -inf, and 1 when the maximum stays), and the V
+// halves feed the FMAs directly.
+template <int G>
+KIE_DI void attn_step2_full(const Dev& D, const u4v k0, const u4v v0, const u4v k1, const u4v v1,
+                            const float (&q)[G][8], float (&mrow)[G], float (&lrow)[G], float (&acc)[G][8]) {
+  const uint32_t vw0[4] = {v0.x, v0.y, v0.z, v0.w}, vw1[4] = {v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float t0 = dot_chunk(k0, f4v{q[h][0], q[h][1], q[h][2], q[h][3]}, f4v{q[h][4], q[h][5], q[h][6], q[h][7]});
+    float t1 = dot_chunk(k1, f4v{q[h][0], q[h][1], q[h][2], q[h][3]}, f4v{q[h][4], q[h][5], q[h][6], q[h][7]});
+    t0 = group_sum(t0, D.lpk);
+    t1 = group_sum(t1, D.lpk);
+    const float mn = fmaxf(mrow[h], fmaxf(t0, t1));
+    const float sc = __builtin_amdgcn_exp2f(mrow[h] - mn);
+    const float p0 = __builtin_amdgcn_exp2f(t0 - mn);
+    const float p1 = __builtin_amdgcn_exp2f(t1 - mn);
+    lrow[h] = __builtin_fmaf(lrow[h], sc, p0 + p1);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc[h][2 * j] = __builtin_fmaf(p1, h2f_lo(vw1[j]), __builtin_fmaf(p0, h2f_lo(vw0[j]), acc[h][2 * j] * sc));
+      acc[h][2 * j + 1] =
+          __builtin_fmaf(p1, h2f_hi(vw1[j]), __builtin_fmaf(p0, h2f_hi(vw0[j]), acc[h][2 * j + 1] * sc));
+    }
+    mrow[h] = mn;
+  }
+}
+
 template <int G>
 KIE_DI void attn_stream(const Dev& D, Cursor& cur, int& slot, Owed& owed, int nst, int ka, int kc,
                         const float (&q)[G][8], float (&mrow)[G], float (&lrow)[G], float (&acc)[G][8]) {
@@ -840,8 +871,14 @@ KIE_DI void attn_stream(const Dev& D, Cursor& cur, int& slot, Owed& owed, int ns
       attn_refill(D, cur, slot, 4, owed);
     }
     slot = ring_add(slot, 4);
-    attn_step<G>(D, x[0], x[1], ka + st * D.kpl + D.kl, kc, q, mrow, lrow, acc);
-    attn_step<G>(D, x[2], x[3], ka + (st + 1) * D.kpl + D.kl, kc, q, mrow, lrow, acc);
+    // (four query heads per KV head would run out of registers with both
+    // forms inlined)
+    if (G <= 2 && ka + (st + 2) * D.kpl <= kc) {
+      attn_step2_full<G>(D, x[0], x[1], x[2], x[3], q, mrow, lrow, acc);
+    } else {
+      attn_step<G>(D, x[0], x[1], ka + st * D.kpl + D.kl, kc, q, mrow, lrow, acc);
+      attn_step<G>(D, x[2], x[3], ka + (st + 1) * D.kpl + D.kl, kc, q, mrow, lrow, acc);
+    }
   }
   if (st < nst) {
     if (rfl(owed.n) == 0) {
