@@ -6,8 +6,9 @@ prompt in seconds, so the full sizes are covered three ways:
 * full-shape models with short prompts, teacher-forced against the oracle
   (cfg1 with its whole 1024-token prompt; cfg2 and the lane variant cfg3 at
   full width and depth; cfg4's width, GQA and vocabulary with two layers);
-* a long-context GQA model whose every wave walks many key steps, against the
-  oracle after a 4096-token prompt;
+* long-context models whose every wave walks many key steps (GQA, and the
+  2.4B model's 20 x 128 attention in a narrow two-layer model), against the
+  oracle after 2400..4096-token prompts;
 * the launch configuration the benchmark times (cfg2, 2048-token prompt
   through the batched prefill, 512 decode steps in one launch): layer-0 keys
   and values at sampled prompt
@@ -85,6 +86,21 @@ def test_long_context_gqa():
     w = gen_weights(cfg, overrides={"wq": 0.05, "wk": 0.05})
     rep, eng = teacher_forced(cfg, w, gen_prompt(cfg), cfg.decode_steps, make_engine, fp16_cache_oracle)
     check(rep, cfg.name)
+    eng.close()
+
+
+@pytest.mark.parametrize("P", [2400, 3000, 4096])
+def test_long_context_mha(P):
+    """20 KV heads of 128 over 256 workgroups (the attention shape of the
+    2.4B model) with 2400..4096 keys: 23..40 keys per wave, 6..10 key steps,
+    so every wave refills its 8-slot ring with key steps during the stream
+    and the split over waves and workgroups moves as the context grows"""
+    cfg = CFG2.with_(name="long-mha", n_layers=2, d_model=512, ffn_dim=1024, vocab=2048, prompt_len=P,
+                     decode_steps=3, seed_index=22)
+    say(f"case long context MHA: P={P} H=Hkv={cfg.n_kv_heads} hd={cfg.head_dim}")
+    w = gen_weights(cfg, overrides={"wq": 0.05, "wk": 0.05})
+    rep, eng = teacher_forced(cfg, w, gen_prompt(cfg), cfg.decode_steps, make_engine, fp16_cache_oracle)
+    check(rep, f"{cfg.name} P={P}")
     eng.close()
 
 
