@@ -599,6 +599,16 @@ kie_status kie_validate_schedule(const kie_model_config* cfg, int32_t nwg, int32
   for (int v : key_owner)
     if (v != 1) return bad("attention key covered zero or several times");
   const kie::LdsPlan lp = kie::lds_plan(m, nwg);
+  // every workgroup's GEMV rows fit the LDS partial sums (and, in the
+  // parallel block, the kept O and residual rows)
+  for (int k : kinds) {
+    for (int w = 0; w < nwg; ++w) {
+      int r0, r1;
+      kie::gemv_rows(m, k, nwg, w, &r0, &r1);
+      if (r1 - r0 > lp.rmax) return bad("GEMV rows of a workgroup exceed the LDS partial-sum rows");
+      if (k == kie::PH_DOWN && 2 * (r1 - r0) > lp.desc - lp.own) return bad("down rows exceed the LDS row store");
+    }
+  }
   for (int g = 0; g < m.Hkv; ++g) {
     const int nrec = kie::attn_owner(m.Hkv, n_ctx, nwg, g, n_ctx - 1) - kie::attn_owner(m.Hkv, n_ctx, nwg, g, 0) + 1;
     if (nrec > lp.max_recs) return bad("more attention records per head than the LDS plan holds");

@@ -315,12 +315,17 @@ KIE_HD LdsPlan lds_plan(const Dims& m, int nwg) {
   // 8g+4..8g+7 at plane 1, position 4g), covering padded_cols(K) elements
   int kmax = imax(imax(imax(padded_cols(m.d), padded_cols(m.H * m.hd)), padded_cols(m.F)), 2 * nwg);
   kmax = (int)align_up((uint64_t)kmax, kBlock);
-  int rmax = 0;
+  // the most GEMV rows any workgroup owns (the splits are uneven), and the
+  // most rows of the down projection (the parallel block keeps those)
+  int rmax = 0, dmax = 0;
   for (int k = 0; k <= PH_LM; ++k) {
     if (k == PH_ATTN) continue;
-    GemvShape s = gemv_shape(m, k);
-    const int units = s.rows / s.unit_rows;
-    rmax = imax(rmax, ((units + nwg - 1) / nwg) * s.unit_rows);
+    for (int w = 0; w < nwg; ++w) {
+      int r0, r1;
+      gemv_rows(m, k, nwg, w, &r0, &r1);
+      rmax = imax(rmax, r1 - r0);
+      if (k == PH_DOWN) dmax = imax(dmax, r1 - r0);
+    }
   }
   // records merged for one head: workgroups meeting that head
   const int max_recs = (nwg + m.Hkv - 1) / m.Hkv + 2;
@@ -344,7 +349,7 @@ KIE_HD LdsPlan lds_plan(const Dims& m, int nwg) {
   p.attn_qkv = p.attn_ml + max_recs * 8;
   const int attn_sz = wrec_sz + max_recs * 8 + 2 * (m.G + 2) * m.hd;
   o += (int)align_up((uint64_t)imax(gemv_sz, attn_sz), 64);
-  p.own = o; o += (int)align_up((uint64_t)2 * ((m.d + nwg - 1) / nwg), 64);
+  p.own = o; o += (int)align_up((uint64_t)2 * dmax, 64);
   p.desc = o; o += kDescInts;
   // phase trace of one step (32-bit stamps, written out at the step's end),
   // when it fits; otherwise stamps go straight to memory

@@ -193,8 +193,13 @@ def test_packer_is_a_permutation(cfg):
         assert not full[:, k:].any(), name
 
 
+# a shape whose O projection (d rows over the workgroups that are not
+# attention mergers) gives a workgroup more rows than any other GEMV does
+O_HEAVY = CFG0.with_(name="o-heavy", d_model=1024, n_heads=4, n_kv_heads=4, head_dim=64, ffn_dim=256, vocab=256)
+
+
 @needs_lib
-@pytest.mark.parametrize("cfg", [CFG0, CFG1, CFG2, CFG3, CFG4], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", [CFG0, CFG1, CFG2, CFG3, CFG4, O_HEAVY], ids=lambda c: c.name)
 def test_schedule_covers_everything(cfg):
     ctxs = sorted({1, 2, 3, 17, cfg.prompt_len, cfg.prompt_len + 1, cfg.max_ctx})
     for nwg in (256, 80, 304):
