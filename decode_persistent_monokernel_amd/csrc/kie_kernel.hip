@@ -119,7 +119,8 @@ KIE_DI void wave_argmax(float& v, int& i) {
     }
   }
 }
-KIE_DI float group_sum(float v, int lpk) {
+// sum over each key's lpk lanes (dl: this lane's index inside its key)
+KIE_DI float group_sum(float v, int lpk, int dl) {
   if (lpk == 16) return row16_sum(v);
   if (lpk == 8) {
     v += dppf<0xB1>(v);
@@ -136,11 +137,15 @@ KIE_DI float group_sum(float v, int lpk) {
     v = row16_sum(v);
     return v + __shfl_xor(v, 16);
   }
-  const int lane = threadIdx.x & 63;
-  const int base = lane - lane % lpk;
-  float s = 0.f;
-  for (int j = 0; j < lpk; ++j) s += __shfl(v, base + j);
-  return s;
+  // other widths: a tree inside the key (lane dl adds lane dl + o while that
+  // is inside the key, o = 1, 2, 4, ...), then the key's first lane holds
+  // the sum and broadcasts it
+  const int lane = (int)(threadIdx.x & 63);
+  for (int o = 1; o < lpk; o *= 2) {
+    const float t = __shfl(v, lane + o);
+    if (dl + o < lpk) v += t;
+  }
+  return __shfl(v, lane - dl);
 }
 
 KIE_DI float h2f_lo(uint32_t u) { return __half2float(__ushort_as_half((unsigned short)(u & 0xFFFF))); }
@@ -811,7 +816,7 @@ KIE_DI void attn_step(const Dev& D, const u4v kx, const u4v vx, int key, int kc,
     float t = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) t = __builtin_fmaf(k8[e], q[h][e], t);
-    t = group_sum(t, D.lpk);
+    t = group_sum(t, D.lpk, D.dl);
     online_update(mrow[h], lrow[h], acc[h], ok ? t : -INFINITY, v8);
   }
 }
@@ -830,8 +835,8 @@ KIE_DI void attn_step2_full(const Dev& D, const u4v k0, const u4v v0, const u4v 
   for (int h = 0; h < G; ++h) {
     float t0 = dot_chunk(k0, f4v{q[h][0], q[h][1], q[h][2], q[h][3]}, f4v{q[h][4], q[h][5], q[h][6], q[h][7]});
     float t1 = dot_chunk(k1, f4v{q[h][0], q[h][1], q[h][2], q[h][3]}, f4v{q[h][4], q[h][5], q[h][6], q[h][7]});
-    t0 = group_sum(t0, D.lpk);
-    t1 = group_sum(t1, D.lpk);
+    t0 = group_sum(t0, D.lpk, D.dl);
+    t1 = group_sum(t1, D.lpk, D.dl);
     const float mn = fmaxf(mrow[h], fmaxf(t0, t1));
     const float sc = __builtin_amdgcn_exp2f(mrow[h] - mn);
     const float p0 = __builtin_amdgcn_exp2f(t0 - mn);
@@ -1184,7 +1189,7 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
               float t = 0.f;
 #pragma unroll
               for (int e = 0; e < 8; ++e) t = __builtin_fmaf(kx[e], q[h][e], t);
-              t = group_sum(t, D.lpk);
+              t = group_sum(t, D.lpk, D.dl);
               if (mine) online_update(mrow[h], lrow[h], acc[h], t, vx);
             }
           }
