@@ -214,13 +214,14 @@ KIE_HD int ceil_div(int a, int b) { return (a + b - 1) / b; }
 // leaves out the attention mergers (the last workgroup of each KV head's
 // group, see attn_segments): they combine their head's partial results after
 // every other workgroup is done with attention, and the O projection's
-// output waits for its slowest producer.  (The parallel block keeps the O
-// rows with the down projection's: a workgroup adds the two outputs of its
-// rows locally.)
+// output waits for its slowest producer.  The parallel block keeps the O
+// rows with the down projection's (a workgroup adds the two outputs of its
+// rows locally), so there both leave the mergers out: their sum is read
+// only layers later, and the mergers catch up on their next QKV rows.
 KIE_HD void gemv_rows(const Dims& m, int kind, int nwg, int wg, int* r0, int* r1) {
   GemvShape s = gemv_shape(m, kind);
   int a, b;
-  if (kind == PH_O && !m.parallel && nwg > m.Hkv) {
+  if ((kind == PH_O || (m.parallel && kind == PH_DOWN)) && nwg > m.Hkv) {
     const int g = split_owner(wg, nwg, m.Hkv);  // the workgroup's KV head group
     int w0, w1;
     split(nwg, m.Hkv, g, &w0, &w1);
