@@ -300,8 +300,8 @@ def main():
             "algorithmic_bytes_per_launch": algo_bytes,
             "kernel_ms": round(kernel_ms, 3),
             "launch_ms_all": [round(x, 3) for x in launch_ms],
-            "kernel": "kie::kie_monokernel<1>" if cfg.n_heads == cfg.n_kv_heads else
-                      f"kie::kie_monokernel<{cfg.n_heads // cfg.n_kv_heads}>",
+            "kernel": f"kie::kie_monokernel<{cfg.n_heads // cfg.n_kv_heads}, "
+                      f"{'false' if cfg.sequential else 'true'}>",
         },
         "tokens_head": [int(t) for t in toks[:8]],
     }

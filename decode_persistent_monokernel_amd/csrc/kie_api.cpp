@@ -15,7 +15,7 @@
 
 extern "C" hipError_t kie_internal_launch(const kie::KParams* kp, int nwg, size_t lds_bytes, hipStream_t stream);
 extern "C" hipError_t kie_internal_zero(void* p, size_t bytes, hipStream_t stream);
-extern "C" hipError_t kie_internal_occupancy(int G, size_t lds_bytes, int* blocks_per_cu);
+extern "C" hipError_t kie_internal_occupancy(int G, int parallel, size_t lds_bytes, int* blocks_per_cu);
 extern "C" hipError_t kie_internal_prefill_chunk(const kie::PrefillArgs* a, hipStream_t stream);
 
 struct kie_ctx {
@@ -260,7 +260,7 @@ kie_status kie_create(const kie_model_config* cfg, int device, kie_ctx** out) {
   }
   if (device >= 0) {
     int per_cu = 0;
-    hipError_t e = kie_internal_occupancy(c->m.G, 0, &per_cu);
+    hipError_t e = kie_internal_occupancy(c->m.G, c->m.parallel, 0, &per_cu);
     if (e != hipSuccess || per_cu < 1) {
       std::fprintf(stderr, "kie_create: kernel does not fit a compute unit (%s)\n",
                    e == hipSuccess ? "occupancy 0" : hipGetErrorString(e));

@@ -919,6 +919,27 @@ KIE_DI void load_gains(const Dev& D, const uint16_t* g, uint16_t (&gr)[kGainRegs
   asm volatile("" ::: "memory");  // issue the loads here, ahead of the poll
 }
 
+// n halves from global memory into LDS as whole 1-KB chunks by LDS DMA,
+// the chunks spread over the waves (a chunk may read past the vector: the
+// packed buffer continues, and the extra halves are never used)
+KIE_DI int gains_pad(int d) { return (d + kBlock - 1) / kBlock * kBlock; }
+KIE_DI void copy_halves(const Dev& D, const uint16_t* g, uint16_t* dst, int n) {
+  const int nch = (n + kBlock - 1) / kBlock;
+#pragma unroll 1
+  for (int c = D.wave; c < nch; c += kWaves)
+    __builtin_amdgcn_global_load_lds((const void*)((const char*)(g + (uint64_t)c * kBlock) + D.lane16),
+                                     (__attribute__((address_space(3))) void*)(dst + c * kBlock), 16, 0, 0);
+}
+// gains kept in LDS (element i at g[i]), read the way load_gains reads them
+KIE_DI void stashed_gains(const Dev& D, const uint16_t* g, uint16_t (&gr)[kGainRegs]) {
+  const int d = D.p->m.d;
+#pragma unroll
+  for (int k = 0; k < kGainRegs; ++k) {
+    const int i = D.tid + k * kThreads;
+    gr[k] = g[i < d ? i : 0];
+  }
+}
+
 // xraw -> xs = g * x / sqrt(mean(x^2) + eps) in the two-plane layout, zero
 // up to the padded row length
 // This thread's elements are read from LDS once, all together (a loop that
@@ -961,7 +982,7 @@ KIE_DI void zero_tail(const Dev& D, float* xs, int K) {
 // ---------------------------------------------------------------------------
 // the kernel
 // ---------------------------------------------------------------------------
-template <int G>
+template <int G, bool PAR>
 __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
   // Two separate LDS objects: the ring, written only by DMAs and read only by
   // the ring-read asm, and everything else.  Keeping them apart lets the compiler
@@ -1009,6 +1030,14 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
   float* wrec = lds_dyn + p.lp.attn_wrec;
   float* mlw = lds_dyn + p.lp.attn_ml;
   float* own = lds_dyn + p.lp.own;  // parallel block: a_l rows, then own residual rows
+  // Parallel block: the O prologue, which waits for the attention output
+  // anyway, also fetches the down projection's input and the next layer's
+  // input and RMSNorm gains.  The down, QKV and gate/up prologues after it
+  // then issue no global loads (theirs would complete behind the ring loads
+  // the waves have just issued).
+  const bool early = PAR && p.lp.hb >= 0;
+  float* const hbs = lds_dyn + (early ? p.lp.hb : 0);
+  uint16_t* const gst = (uint16_t*)(lds_dyn + (early ? p.lp.gst : 0));
   int* wgrows = D.desc + kWaves * kWaveDesc;
 
   if (D.tid == 0) *abort_flag(D) = 0;
@@ -1097,7 +1126,7 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
       }
     }
     wg_sync();
-    if (p.m.parallel) {
+    if (PAR) {
       const int r0 = wgrows[2 * 3], nr = wgrows[2 * 3 + 1];
       for (int t = D.tid; t < nr; t += kThreads) own[nr + t] = xraw[r0 + t];
       wg_sync();
@@ -1116,7 +1145,7 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
     const int nph = nphases(p, s);
     for (int ph = 0; ph < nph; ++ph) {
       const bool is_lm = ph == 5 * L;
-      const int kind = is_lm ? PH_LM : phase_kind(p.m.parallel, ph % 5);
+      const int kind = is_lm ? PH_LM : phase_kind(PAR, ph % 5);
       const int l = is_lm ? L : ph / 5;
       const uint16_t* Wl = p.W + (uint64_t)(is_lm ? 0 : l) * p.pl.layer_stride;
 
@@ -1374,8 +1403,13 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
       // prologue: the input vector
       uint16_t gr[kGainRegs];
       float2 rope_cs = make_float2(1.f, 0.f);
+      const bool staged = early && l > 0 && !is_lm;  // input and gains fetched by the last O prologue
       if (kind == PH_QKV) {
-        load_gains(D, Wl + p.pl.attn_norm, gr);
+        if (staged) {
+          stashed_gains(D, gst, gr);
+        } else {
+          load_gains(D, Wl + p.pl.attn_norm, gr);
+        }
         // this thread's RoPE factors for the epilogue, fetched ahead too
         // (unconditionally, from a clamped index: see load_gains)
         {
@@ -1385,27 +1419,48 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
           rope_cs = D.rope[(uint64_t)pos * (hd / 2) + i];
         }
         asm volatile("" ::: "memory");
-        if (p.m.parallel ? (l > p.m.delay) : (l > 0)) {
-          const int xi = p.m.parallel ? l : 2 * l;
+        if (!staged && (PAR ? (l > p.m.delay) : (l > 0))) {
+          const int xi = PAR ? l : 2 * l;
           poll_to_lds<false>(D, D.X + (uint64_t)xi * d, xraw, d, epoch);
           wg_sync();
           if (aborted(D)) { __builtin_amdgcn_s_waitcnt(kWaitAllVm); return; }
         }
         rmsnorm_to_xs(D, xraw, gr, xs);
       } else if (kind == PH_GU) {
-        load_gains(D, Wl + p.pl.mlp_norm, gr);
-        if (!p.m.parallel) {
+        if (staged) {
+          stashed_gains(D, gst + gains_pad(d), gr);
+        } else {
+          load_gains(D, Wl + p.pl.mlp_norm, gr);
+        }
+        if (!PAR) {
           poll_to_lds<false>(D, D.X + (uint64_t)(2 * l + 1) * d, xraw, d, epoch);
           wg_sync();
           if (aborted(D)) { __builtin_amdgcn_s_waitcnt(kWaitAllVm); return; }
         }
         rmsnorm_to_xs(D, xraw, gr, xs);
       } else if (kind == PH_O) {
+        if (early) {
+          const bool next = l + 1 < L;
+          if (next) {
+            copy_halves(D, Wl + p.pl.layer_stride + p.pl.attn_norm, gst, d);
+            copy_halves(D, Wl + p.pl.layer_stride + p.pl.mlp_norm, gst + gains_pad(d), d);
+          }
+          if (rfl(wgrows[2 * gemv_index(PH_DOWN) + 1]) > 0) {
+            poll_to_lds<true>(D, D.HB + (uint64_t)l * F, hbs, F, epoch);
+            zero_tail(D, hbs, F);
+          }
+          if (next && l + 1 > p.m.delay) poll_to_lds<false>(D, D.X + (uint64_t)(l + 1) * d, xraw, d, epoch);
+        }
         poll_to_lds<true>(D, D.OB + (uint64_t)l * qd, xs, qd, epoch);
         zero_tail(D, xs, qd);
+        // (loads complete in order: the gain copies, issued before the polls,
+        // have landed; the wait only makes it explicit)
+        if (early) __builtin_amdgcn_s_waitcnt(kWaitAllVm);
       } else if (kind == PH_DOWN) {
-        poll_to_lds<true>(D, D.HB + (uint64_t)l * F, xs, F, epoch);
-        zero_tail(D, xs, F);
+        if (!early) {
+          poll_to_lds<true>(D, D.HB + (uint64_t)l * F, xs, F, epoch);
+          zero_tail(D, xs, F);
+        }
       } else {  // LM
         load_gains(D, p.W + p.pl.final_norm, gr);
         poll_to_lds<false>(D, D.X + (uint64_t)(2 * L) * d, xraw, d, epoch);
@@ -1420,7 +1475,8 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
 
       {
         const int* gd = D.desc + D.wave * kWaveDesc + 8 * gi;
-        gemv_stream(D, cur, slot, xs, part, rfl(gd[2]), rfl(gd[3]), rfl(gd[4]), rfl(gd[5]));
+        const float* gin = (early && kind == PH_DOWN) ? hbs : xs;
+        gemv_stream(D, cur, slot, gin, part, rfl(gd[2]), rfl(gd[3]), rfl(gd[4]), rfl(gd[5]));
       }
       stamp(D, s, ph, 2);
       wg_sync();
@@ -1486,7 +1542,7 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
           float y = 0.f;
 #pragma unroll
           for (int w = 0; w < kWaves; ++w) y += part[t * kWaves + w];
-          if (p.m.parallel) {
+          if (PAR) {
             own[t] = y;  // a_l for the rows this workgroup owns
           } else {
             ll_storef(D.X + (uint64_t)(2 * l + 1) * d + r0 + t, xraw[r0 + t] + y, epoch);
@@ -1497,7 +1553,7 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
           float y = 0.f;
 #pragma unroll
           for (int w = 0; w < kWaves; ++w) y += part[t * kWaves + w];
-          if (p.m.parallel) {
+          if (PAR) {
             // P_l = a_l + m_l reaches the residual of layer l + delay + 1
             const float xn = own[nrows + t] + (own[t] + y);
             own[nrows + t] = xn;
@@ -1635,17 +1691,23 @@ __global__ void kie_zero_kernel(uint4* p, uint64_t n16) {
 // ---------------------------------------------------------------------------
 // host-side launch helpers (called by the C-ABI in kie_api.cpp)
 // ---------------------------------------------------------------------------
-static const void* kie_kernel_for(int G) {
-  switch (G) {
-    case 1: return (const void*)&kie::kie_monokernel<1>;
-    case 2: return (const void*)&kie::kie_monokernel<2>;
-    case 4: return (const void*)&kie::kie_monokernel<4>;
+// one kernel per (query heads per KV head, block kind): the sequential and
+// the parallel block are separate instantiations, so neither carries the
+// other's branches
+static const void* kie_kernel_for(int G, int parallel) {
+  switch (G * 2 + (parallel ? 1 : 0)) {
+    case 2: return (const void*)&kie::kie_monokernel<1, false>;
+    case 3: return (const void*)&kie::kie_monokernel<1, true>;
+    case 4: return (const void*)&kie::kie_monokernel<2, false>;
+    case 5: return (const void*)&kie::kie_monokernel<2, true>;
+    case 8: return (const void*)&kie::kie_monokernel<4, false>;
+    case 9: return (const void*)&kie::kie_monokernel<4, true>;
     default: return nullptr;
   }
 }
 
 extern "C" hipError_t kie_internal_launch(const kie::KParams* kp, int nwg, size_t lds_bytes, hipStream_t stream) {
-  const void* fn = kie_kernel_for(kp->m.G);
+  const void* fn = kie_kernel_for(kp->m.G, kp->m.parallel);
   if (!fn) return hipErrorInvalidValue;
   (void)lds_bytes;  // all LDS is static
   void* args[] = {(void*)kp};
@@ -1662,8 +1724,8 @@ extern "C" hipError_t kie_internal_zero(void* p, size_t bytes, hipStream_t strea
   return hipGetLastError();
 }
 
-extern "C" hipError_t kie_internal_occupancy(int G, size_t lds_bytes, int* blocks_per_cu) {
-  const void* fn = kie_kernel_for(G);
+extern "C" hipError_t kie_internal_occupancy(int G, int parallel, size_t lds_bytes, int* blocks_per_cu) {
+  const void* fn = kie_kernel_for(G, parallel);
   if (!fn) return hipErrorInvalidValue;
   (void)lds_bytes;
   return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, fn, kie::kThreads, 0);

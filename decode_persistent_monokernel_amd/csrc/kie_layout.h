@@ -306,6 +306,11 @@ KIE_HD int trace_slots(int L) { return 5 * L + 2; }
 // LDS plan (in floats)
 struct LdsPlan {
   int xraw, big, gemv_xs, gemv_part, attn_wrec, attn_ml, attn_qkv, own, desc, trace;
+  // parallel block: the down projection's input (two planes, kmax floats) and
+  // the next layer's two RMSNorm gain vectors (whole 1-KB chunks: attention
+  // gains at half 0, MLP gains at half align(d, 512)), both fetched in
+  // the O prologue; -1 when they do not fit
+  int hb, gst;
   int total_floats;
   int kmax, rmax, max_recs;
 };
@@ -352,6 +357,18 @@ KIE_HD LdsPlan lds_plan(const Dims& m, int nwg) {
   o += (int)align_up((uint64_t)imax(gemv_sz, attn_sz), 64);
   p.own = o; o += (int)align_up((uint64_t)2 * dmax, 64);
   p.desc = o; o += kDescInts;
+  p.hb = -1;
+  p.gst = -1;
+  if (m.parallel) {
+    const int hb = (int)align_up((uint64_t)o, 64);
+    const int gst = hb + kmax;
+    const int end = gst + (int)align_up((uint64_t)m.d, kBlock);  // 2 x align(d, 512) halves
+    if (end <= kMainFloats) {
+      p.hb = hb;
+      p.gst = gst;
+      o = end;
+    }
+  }
   // phase trace of one step (32-bit stamps, written out at the step's end),
   // when it fits; otherwise stamps go straight to memory
   p.trace = -1;
