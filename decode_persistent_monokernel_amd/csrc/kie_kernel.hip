@@ -973,6 +973,41 @@ KIE_DI void rmsnorm_to_xs(const Dev& D, const float* xraw, const uint16_t (&gr)[
   }
 }
 
+// the same normalisation for two gain vectors at once (the parallel block's
+// QKV and gate/up read the same x_l): xa with gains ga, xb with gains gb
+KIE_DI void rmsnorm_to_xs2(const Dev& D, const float* xraw, const uint16_t (&ga)[kGainRegs], float* xa,
+                           const uint16_t (&gb)[kGainRegs], float* xb) {
+  const KParams& p = *D.p;
+  const int d = p.m.d;
+  const int t = opaque(D.tid);
+  float xv[kGainRegs];
+#pragma unroll
+  for (int k = 0; k < kGainRegs; ++k) {
+    const int i = t + k * kThreads;
+    xv[k] = xraw[i < d ? i : 0];
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int k = 0; k < kGainRegs; ++k) ss += t + k * kThreads < d ? xv[k] * xv[k] : 0.f;
+  ss = wave_sum(ss);
+  if (D.lane == 0) D.sh->redf[D.wave] = ss;
+  wg_sync();
+  float tot = 0.f;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) tot += D.sh->redf[w];
+  const float inv = 1.0f / sqrtf(tot / (float)d + p.m.eps);
+  const int padded = padded_cols(d);
+#pragma unroll
+  for (int k = 0; k < kGainRegs; ++k) {
+    const int i = t + k * kThreads;
+    if (i < padded) {
+      const float xn = xv[k] * inv;
+      xa[xs_pos(i, D.plane)] = i < d ? xn * hbits2f(ga[k]) : 0.f;
+      xb[xs_pos(i, D.plane)] = i < d ? xn * hbits2f(gb[k]) : 0.f;
+    }
+  }
+}
+
 // the zero columns of a padded row (padded_cols(K) > K)
 KIE_DI void zero_tail(const Dev& D, float* xs, int K) {
   const int padded = padded_cols(K);
@@ -1126,9 +1161,18 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
       }
     }
     wg_sync();
+    // parallel block: this thread's RoPE factors for every layer's QKV
+    // epilogue (the position and the workgroup's QKV rows are the same in
+    // every layer), so that no QKV prologue loads them
+    float2 rope_step = make_float2(1.f, 0.f);
     if (PAR) {
       const int r0 = wgrows[2 * 3], nr = wgrows[2 * 3 + 1];
       for (int t = D.tid; t < nr; t += kThreads) own[nr + t] = xraw[r0 + t];
+      const int qr0 = wgrows[2 * gemv_index(PH_QKV)], qn = wgrows[2 * gemv_index(PH_QKV) + 1];
+      const int rr = qr0 + 2 * D.tid;
+      const bool mine = 2 * D.tid < qn && rr < qd + kvd;
+      const int i = mine ? ((rr < qd ? rr : rr - qd) % hd) >> 1 : 0;
+      rope_step = D.rope[(uint64_t)pos * (hd / 2) + i];
       wg_sync();
     }
 
@@ -1412,7 +1456,9 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
         }
         // this thread's RoPE factors for the epilogue, fetched ahead too
         // (unconditionally, from a clamped index: see load_gains)
-        {
+        if (PAR) {
+          rope_cs = rope_step;
+        } else {
           const int rr = r0 + 2 * D.tid;
           const bool mine = 2 * D.tid < nrows && rr < qd + kvd;
           const int i = mine ? ((rr < qd ? rr : rr - qd) % hd) >> 1 : 0;
@@ -1425,7 +1471,20 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
           wg_sync();
           if (aborted(D)) { __builtin_amdgcn_s_waitcnt(kWaitAllVm); return; }
         }
-        rmsnorm_to_xs(D, xraw, gr, xs);
+        if (early) {
+          // gate/up's input too, into the down input's area (idle until O)
+          uint16_t gg[kGainRegs];
+          if (staged) {
+            stashed_gains(D, gst + gains_pad(d), gg);
+          } else {
+            load_gains(D, Wl + p.pl.mlp_norm, gg);
+          }
+          rmsnorm_to_xs2(D, xraw, gr, xs, gg, hbs);
+        } else {
+          rmsnorm_to_xs(D, xraw, gr, xs);
+        }
+      } else if (kind == PH_GU && early) {
+        // input prepared by the QKV prologue
       } else if (kind == PH_GU) {
         if (staged) {
           stashed_gains(D, gst + gains_pad(d), gr);
@@ -1475,7 +1534,7 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
 
       {
         const int* gd = D.desc + D.wave * kWaveDesc + 8 * gi;
-        const float* gin = (early && kind == PH_DOWN) ? hbs : xs;
+        const float* gin = (early && (kind == PH_DOWN || kind == PH_GU)) ? hbs : xs;
         gemv_stream(D, cur, slot, gin, part, rfl(gd[2]), rfl(gd[3]), rfl(gd[4]), rfl(gd[5]));
       }
       stamp(D, s, ph, 2);
