@@ -405,6 +405,69 @@ KIE_DI void poll_to_lds(const Dev& D, const u64* src, float* dst, int n, uint32_
   }
 }
 
+// Up to three vectors polled in one round trip: word j of the concatenation
+// (j = tid + k * kThreads, k < K) is loaded for all k before any is waited
+// for, and only stale words are loaded again.  Returns false on abort or
+// time-out (as poll_words).  The caller checks n0 + n1 + n2 <= K * kThreads.
+struct PollSeg {
+  const u64* src;
+  float* dst;
+  int n, swz;
+};
+template <int K>
+KIE_DI bool poll_multi(const Dev& D, const PollSeg (&sg)[3], uint32_t epoch) {
+  const int n01 = sg[0].n + sg[1].n, nt = n01 + sg[2].n;
+  u64 v[K];
+  auto addr = [&](int j) -> const u64* {
+    return j < sg[0].n ? sg[0].src + j : j < n01 ? sg[1].src + (j - sg[0].n) : sg[2].src + (j - n01);
+  };
+  uint32_t mask = 0;
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const int j = D.tid + k * kThreads;
+    if (j < nt) {
+      mask |= 1u << k;
+      v[k] = ll_load(addr(j));
+    }
+  }
+  uint64_t t0 = 0;
+  for (int it = 0;; ++it) {
+    uint32_t stale = 0;
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+      if ((mask & (1u << k)) && ll_epoch(v[k]) != epoch) stale |= 1u << k;
+    if (!stale) break;
+    if (it == 0) t0 = wall_clock64();
+    if ((it & 15) == 15) {
+      if (abort_seen(D)) return false;
+      if (__hip_atomic_load(&D.state[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+        set_abort(D);
+        return false;
+      }
+      if (wall_clock64() - t0 > D.p->timeout_ticks) {
+        raise_status(D, DEV_TIMEOUT);
+        return false;
+      }
+    }
+    __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+      if (stale & (1u << k)) v[k] = ll_load(addr(D.tid + k * kThreads));
+  }
+  const int plane = D.plane;
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const int j = D.tid + k * kThreads;
+    if (j < nt) {
+      const int s = j < sg[0].n ? 0 : j < n01 ? 1 : 2;
+      const int i = j - (s == 0 ? 0 : s == 1 ? sg[0].n : n01);
+      sg[s].dst[sg[s].swz ? xs_pos(i, plane) : i] = ll_f(v[k]);
+    }
+  }
+  return true;
+}
+constexpr int kMultiPoll1 = 14, kMultiPoll2 = 10;  // words per thread of the O prologue's two rounds
+
 // ---------------------------------------------------------------------------
 // work descriptors (in LDS, see kie_layout.h)
 // ---------------------------------------------------------------------------
@@ -1504,13 +1567,31 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
             copy_halves(D, Wl + p.pl.layer_stride + p.pl.attn_norm, gst, d);
             copy_halves(D, Wl + p.pl.layer_stride + p.pl.mlp_norm, gst + gains_pad(d), d);
           }
-          if (rfl(wgrows[2 * gemv_index(PH_DOWN) + 1]) > 0) {
-            poll_to_lds<true>(D, D.HB + (uint64_t)l * F, hbs, F, epoch);
-            zero_tail(D, hbs, F);
+          const bool want_hb = rfl(wgrows[2 * gemv_index(PH_DOWN) + 1]) > 0;
+          const bool want_x = next && l + 1 > p.m.delay;
+          // two round trips: down's input, then the next x and the
+          // attention output together (when they fit the batches)
+          const PollSeg s1[3] = {{D.HB + (uint64_t)l * F, hbs, want_hb ? F : 0, 1},
+                                 {D.HB, hbs, 0, 1},
+                                 {D.HB, hbs, 0, 1}};
+          const PollSeg s2[3] = {{D.X + (uint64_t)(l + 1) * d, xraw, want_x ? d : 0, 0},
+                                 {D.OB + (uint64_t)l * qd, xs, qd, 1},
+                                 {D.OB, xs, 0, 1}};
+          if (s1[0].n <= kMultiPoll1 * kThreads) {
+            (void)poll_multi<kMultiPoll1>(D, s1, epoch);
+          } else {
+            poll_to_lds<true>(D, s1[0].src, hbs, F, epoch);
           }
-          if (next && l + 1 > p.m.delay) poll_to_lds<false>(D, D.X + (uint64_t)(l + 1) * d, xraw, d, epoch);
+          if (s2[0].n + s2[1].n <= kMultiPoll2 * kThreads) {
+            (void)poll_multi<kMultiPoll2>(D, s2, epoch);
+          } else {
+            if (want_x) poll_to_lds<false>(D, s2[0].src, xraw, d, epoch);
+            poll_to_lds<true>(D, s2[1].src, xs, qd, epoch);
+          }
+          if (want_hb) zero_tail(D, hbs, F);
+        } else {
+          poll_to_lds<true>(D, D.OB + (uint64_t)l * qd, xs, qd, epoch);
         }
-        poll_to_lds<true>(D, D.OB + (uint64_t)l * qd, xs, qd, epoch);
         zero_tail(D, xs, qd);
         // (loads complete in order: the gain copies, issued before the polls,
         // have landed; the wait only makes it explicit)
