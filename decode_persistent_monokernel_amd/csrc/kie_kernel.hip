@@ -466,7 +466,7 @@ KIE_DI bool poll_multi(const Dev& D, const PollSeg (&sg)[3], uint32_t epoch) {
   }
   return true;
 }
-constexpr int kMultiPoll1 = 14, kMultiPoll2 = 10;  // words per thread of the O prologue's two rounds
+constexpr int kMultiPoll1 = 14, kMultiPoll2 = 10;  // words per thread of a batched poll (one, two vectors)
 
 // ---------------------------------------------------------------------------
 // work descriptors (in LDS, see kie_layout.h)
@@ -1133,7 +1133,7 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
   // input and RMSNorm gains.  The down, QKV and gate/up prologues after it
   // then issue no global loads (theirs would complete behind the ring loads
   // the waves have just issued).
-  const bool early = PAR && p.lp.hb >= 0;
+  const bool early = PAR && G <= 2 && p.lp.hb >= 0;  // (four query heads per KV head: too many registers)
   float* const hbs = lds_dyn + (early ? p.lp.hb : 0);
   uint16_t* const gst = (uint16_t*)(lds_dyn + (early ? p.lp.gst : 0));
   int* wgrows = D.desc + kWaves * kWaveDesc;
@@ -1582,7 +1582,7 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
           } else {
             poll_to_lds<true>(D, s1[0].src, hbs, F, epoch);
           }
-          if (s2[0].n + s2[1].n <= kMultiPoll2 * kThreads) {
+          if (G <= 2 && s2[0].n + s2[1].n <= kMultiPoll2 * kThreads) {
             (void)poll_multi<kMultiPoll2>(D, s2, epoch);
           } else {
             if (want_x) poll_to_lds<false>(D, s2[0].src, xraw, d, epoch);
@@ -1598,7 +1598,14 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
         if (early) __builtin_amdgcn_s_waitcnt(kWaitAllVm);
       } else if (kind == PH_DOWN) {
         if (!early) {
-          poll_to_lds<true>(D, D.HB + (uint64_t)l * F, xs, F, epoch);
+          // one batch of loads when it fits (a second batch would be issued
+          // only once the first is complete: one more round trip)
+          const PollSeg sd[3] = {{D.HB + (uint64_t)l * F, xs, F, 1}, {D.HB, xs, 0, 1}, {D.HB, xs, 0, 1}};
+          if (!PAR && G == 1 && F <= kMultiPoll1 * kThreads) {  // (more heads per KV head: too many registers)
+            (void)poll_multi<kMultiPoll1>(D, sd, epoch);
+          } else {
+            poll_to_lds<true>(D, D.HB + (uint64_t)l * F, xs, F, epoch);
+          }
           zero_tail(D, xs, F);
         }
       } else {  // LM
