@@ -102,6 +102,19 @@ def test_lane_block_small():
     eng.close()
 
 
+def test_lane_block_wide_ffn():
+    """the parallel block when its O prologue cannot stage the down
+    projection's input and the next layer's gains (a 12288-wide FFN leaves no
+    LDS for them): the down, QKV and gate/up prologues fetch their own"""
+    cfg = CFG0.with_(name="lanes-wide", n_layers=4, n_lanes=2, lane_delay=1, sequential=False, ffn_dim=12288,
+                     seed_index=14, prompt_len=9, decode_steps=8)
+    say("case parallel block, delay 1, FFN 12288 (no staging in the O prologue)")
+    w = gen_weights(cfg, overrides={"wq": 0.1, "wk": 0.1})
+    rep, eng = teacher_forced(cfg, w, gen_prompt(cfg), cfg.decode_steps, make_engine, oracle_fp16_cache)
+    check(rep, "lanes-wide")
+    eng.close()
+
+
 def test_single_token_prompt_and_free_running():
     cfg = CFG0.with_(seed_index=13, prompt_len=1, decode_steps=20)
     say("case prompt of one token, free-running greedy")
