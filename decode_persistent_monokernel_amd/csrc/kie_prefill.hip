@@ -5,10 +5,11 @@
 // dense [C x K] x [K x N] products, so each weight is read once per chunk
 // instead of once per token.
 //
-// Arithmetic matches the decode kernel's: fp32 activations, fp16 weights
-// widened exactly, fp32 accumulation (v_mfma_f32_32x32x2f32), the same RMSNorm,
-// RoPE, fp16 rounding of cached K and V, exp2-domain softmax and SwiGLU
-// formulas.  Only summation orders differ.
+// Arithmetic matches the decode kernel's to fp32 accuracy: fp32 activations
+// (in the weight GEMMs carried as fp16 hi + lo pairs on the fp16 matrix
+// cores), fp16 weights, fp32 accumulation, the same RMSNorm, RoPE, fp16
+// rounding of cached K and V, exp2-domain softmax and SwiGLU formulas.  Only
+// summation orders (and the ~2^-22 split error) differ.
 //
 // Kernels, launched in stream order per chunk and layer:
 //   embed -> [rmsnorm -> gemm(QKV) -> rope_kv -> attention -> gemm(O, +X)
@@ -74,19 +75,28 @@ __global__ void __launch_bounds__(kRowThreads) rmsnorm(float* Y, int ldy, const 
 // columns n0 + 32w .. +32 and both 32-row halves, two 32x32 accumulators.
 // The next k tile is fetched into registers while the current one is
 // multiplied from LDS (double-buffered).
-constexpr int BM = 64, BN = 128, BK = 32, LDP = BK + 1;
+constexpr int BM = 64, BN = 128, BK = 32;
+
+// The product runs on the fp16 matrix cores to fp32 accuracy: each fp32
+// activation a is split into hi = fp16(a) and lo = fp16(a - hi), so that
+// hi + lo = a to about 2^-22 relative, and the weights are fp16 already;
+// hi * W and lo * W accumulate in fp32 (v_mfma_f32_32x32x8f16, two per
+// k-step of 8).  The split happens once, when a tile is staged in LDS.  LDS
+// rows hold 36 halves (72 bytes), so that the 32 rows a fragment read
+// touches start in different banks.
+typedef _Float16 h4v __attribute__((ext_vector_type(4)));
+constexpr int HP = BK + 4;
 
 template <bool ADD>
-__global__ void __launch_bounds__(256) gemm(float* Out, int ldo, const float* A, int lda, const uint16_t* Wm,
-                                            int M, int N, int K) {
-  __shared__ float As[2][BM][LDP];
-  __shared__ float Bs[2][BN][LDP];
+__global__ void __launch_bounds__(256) gemm16(float* Out, int ldo, const float* A, int lda, const uint16_t* Wm,
+                                              int M, int N, int K) {
+  __shared__ _Float16 Ah[2][BM][HP];
+  __shared__ _Float16 Al[2][BM][HP];
+  __shared__ uint16_t Bh[2][BN][HP];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
   const int nkt = (K + BK - 1) / BK;
   const int cb = col_blocks(K);
-  // loads of this thread: A rows ar and ar + 32, columns ak .. ak + 3;
-  // B row bn (packed), columns bk .. bk + 15
   const int ar = tid >> 3, ak = (tid & 7) * 4;
   const int bn = tid >> 1, bk = (tid & 1) * 16;
   float4 ra[2];
@@ -123,19 +133,21 @@ __global__ void __launch_bounds__(256) gemm(float* Out, int ldo, const float* A,
   auto stash = [&](int buf) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      float* d = &As[buf][ar + 32 * h][ak];
-      d[0] = ra[h].x;
-      d[1] = ra[h].y;
-      d[2] = ra[h].z;
-      d[3] = ra[h].w;
-    }
-    float* d = &Bs[buf][bn][bk];
-    const uint32_t w[8] = {rb[0].x, rb[0].y, rb[0].z, rb[0].w, rb[1].x, rb[1].y, rb[1].z, rb[1].w};
+      const float x[4] = {ra[h].x, ra[h].y, ra[h].z, ra[h].w};
+      h4v hi, lo;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      d[2 * i] = h2f((uint16_t)(w[i] & 0xFFFF));
-      d[2 * i + 1] = h2f((uint16_t)(w[i] >> 16));
+      for (int i = 0; i < 4; ++i) {
+        hi[i] = (_Float16)x[i];
+        lo[i] = (_Float16)(x[i] - (float)hi[i]);
+      }
+      *(h4v*)&Ah[buf][ar + 32 * h][ak] = hi;
+      *(h4v*)&Al[buf][ar + 32 * h][ak] = lo;
     }
+    uint2* d = (uint2*)&Bh[buf][bn][bk];
+    d[0] = make_uint2(rb[0].x, rb[0].y);
+    d[1] = make_uint2(rb[0].z, rb[0].w);
+    d[2] = make_uint2(rb[1].x, rb[1].y);
+    d[3] = make_uint2(rb[1].z, rb[1].w);
   };
   f16v acc[2];
 #pragma unroll
@@ -150,12 +162,17 @@ __global__ void __launch_bounds__(256) gemm(float* Out, int ldo, const float* A,
     const int buf = kt & 1;
     if (kt + 1 < nkt) fetch(kt + 1);
 #pragma unroll
-    for (int kk = 0; kk < BK; kk += 2) {
-      const float b = Bs[buf][wave * 32 + li][kk + lk];
-      const float a0 = As[buf][li][kk + lk];
-      const float a1 = As[buf][32 + li][kk + lk];
-      acc[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b, acc[0], 0, 0, 0);
-      acc[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b, acc[1], 0, 0, 0);
+    for (int kk = 0; kk < BK; kk += 8) {
+      // operands: lane l holds row (or column) l % 32, k = kk + 4 (l / 32) .. +3
+      const int kq = kk + 4 * lk;
+      const h4v b = *(const h4v*)&Bh[buf][wave * 32 + li][kq];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const h4v ah = *(const h4v*)&Ah[buf][32 * i + li][kq];
+        const h4v al = *(const h4v*)&Al[buf][32 * i + li][kq];
+        acc[i] = __builtin_amdgcn_mfma_f32_32x32x8f16(ah, b, acc[i], 0, 0, 0);
+        acc[i] = __builtin_amdgcn_mfma_f32_32x32x8f16(al, b, acc[i], 0, 0, 0);
+      }
     }
     if (kt + 1 < nkt) stash(buf ^ 1);
     __syncthreads();
@@ -476,9 +493,9 @@ static hipError_t launch_gemm(bool add, float* Out, int ldo, const float* A, int
                               int K, hipStream_t st) {
   const dim3 grid((N + pf::BN - 1) / pf::BN, (M + pf::BM - 1) / pf::BM);
   if (add) {
-    hipLaunchKernelGGL(pf::gemm<true>, grid, dim3(256), 0, st, Out, ldo, A, lda, Wm, M, N, K);
+    hipLaunchKernelGGL(pf::gemm16<true>, grid, dim3(256), 0, st, Out, ldo, A, lda, Wm, M, N, K);
   } else {
-    hipLaunchKernelGGL(pf::gemm<false>, grid, dim3(256), 0, st, Out, ldo, A, lda, Wm, M, N, K);
+    hipLaunchKernelGGL(pf::gemm16<false>, grid, dim3(256), 0, st, Out, ldo, A, lda, Wm, M, N, K);
   }
   return hipGetLastError();
 }
