@@ -29,6 +29,18 @@ constexpr int kRowThreads = 256;
 
 __device__ __forceinline__ float h2f(uint16_t u) { return __half2float(__ushort_as_half(u)); }
 
+// fp32 values as fp16 pairs for the fp16 matrix cores: hi = fp16(x),
+// lo = fp16(x - hi), hi + lo = x to about 2^-22 relative
+typedef _Float16 h4v __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void split4(const float4 x, h4v& hi, h4v& lo) {
+  const float v[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    hi[i] = (_Float16)v[i];
+    lo[i] = (_Float16)(v[i] - (float)hi[i]);
+  }
+}
+
 __device__ __forceinline__ float block_sum(float v, float* red) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
@@ -84,7 +96,6 @@ constexpr int BM = 64, BN = 128, BK = 32;
 // k-step of 8).  The split happens once, when a tile is staged in LDS.  LDS
 // rows hold 36 halves (72 bytes), so that the 32 rows a fragment read
 // touches start in different banks.
-typedef _Float16 h4v __attribute__((ext_vector_type(4)));
 constexpr int HP = BK + 4;
 
 template <bool ADD>
@@ -133,13 +144,8 @@ __global__ void __launch_bounds__(256) gemm16(float* Out, int ldo, const float* 
   auto stash = [&](int buf) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const float x[4] = {ra[h].x, ra[h].y, ra[h].z, ra[h].w};
       h4v hi, lo;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        hi[i] = (_Float16)x[i];
-        lo[i] = (_Float16)(x[i] - (float)hi[i]);
-      }
+      split4(ra[h], hi, lo);
       *(h4v*)&Ah[buf][ar + 32 * h][ak] = hi;
       *(h4v*)&Al[buf][ar + 32 * h][ak] = lo;
     }
@@ -313,12 +319,14 @@ __global__ void __launch_bounds__(256) attention(float* Ao, const float* Qn, con
 
 // Causal attention on the matrix cores (flash-attention order): a workgroup
 // takes 64 query tokens of one head, wave w the 16 tokens 16w .. 16w+15.  Key
-// blocks of 64 are staged in LDS as fp32 (K and V of the head's KV head,
-// zero past the last key) and shared by the four waves.  Per block, with
-// v_mfma_f32_16x16x4f32: S = Q K^T (16 x 64 per wave, the log2-domain scores),
-// masked above the diagonal; a row-wise online softmax (max and sum over the
-// 16 lanes holding a row's columns, DPP); P goes through LDS into the A-operand
-// layout; O += P V.  fp32 throughout, like the decode kernel's attention.
+// blocks of 64 are staged in LDS as the cache holds them, fp16 (K as is, V
+// transposed; zero past the last key) and shared by the four waves.  Per
+// block, with v_mfma_f32_16x16x16f16: S = Q K^T (16 x 64 per wave, the
+// log2-domain scores), masked above the diagonal; a row-wise online softmax
+// (max and sum over the 16 lanes holding a row's columns, DPP); P goes through
+// LDS into the A-operand layout; O += P V.  Q and P enter the products as
+// fp16 hi + lo pairs (split4), so both products keep fp32 accuracy, like the
+// decode kernel's attention.
 // For hd a multiple of 16 and at most 128 (larger heads use `attention`).
 typedef float f4v __attribute__((ext_vector_type(4)));
 constexpr int FQ = 64, FK = 64;  // query tokens and keys per block
@@ -341,25 +349,28 @@ __device__ __forceinline__ float row16_add(float v) {
 template <int HD>
 __global__ void __launch_bounds__(256) attention_mfma(float* Ao, const float* Qn, const uint16_t* kv, Dims m, int l,
                                                       int pos0, int C) {
-  constexpr int KS = HD + 4;   // K row stride (floats): conflict-free B-operand reads
-  constexpr int VS = HD + 16;  // V row stride
-  constexpr int PS = FK + 4;   // P row stride
-  constexpr int NS = HD / 4;   // k-steps of Q K^T
+  constexpr int KS = HD + 4;  // K row stride (halves): a fragment's 16 rows start in different banks
+  constexpr int VT = FK + 4;  // transposed V row stride (halves)
+  constexpr int PS = FK + 4;  // P row stride (floats)
+  constexpr int NS = HD / 16;  // k-steps of Q K^T
   constexpr int NU = HD / 16;  // 16-wide output column tiles
-  __shared__ float Ks[FK * KS];
-  __shared__ float Vs[FK * VS];
+  __shared__ uint16_t Ks[FK * KS];  // K[key][dim], fp16 as stored
+  __shared__ uint16_t Vt[HD * VT];  // V[key][dim] transposed: Vt[dim][key]
   __shared__ float Ps[4][16 * PS];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int lr = lane & 15, lq = lane >> 4;
   const int qb = blockIdx.x, h = blockIdx.y;
   const int H = m.H, qd = H * HD, g = h / m.G;
   const int t0 = qb * FQ + wave * 16;  // this wave's first token in the chunk
-  // Q fragments: lane holds Q[token t0 + lr][dim 4s + lq] for s < NS
-  float qf[NS];
+  // Q fragments: lane holds Q[token t0 + lr][dims 16 s + 4 lq .. +3], split
+  // into fp16 hi and lo parts
+  h4v qh[NS], ql[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     const int t = t0 + lr;
-    qf[s] = t < C ? Qn[(uint64_t)t * qd + (uint64_t)h * HD + 4 * s + lq] : 0.f;
+    float4 q = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (t < C) q = *(const float4*)(Qn + (uint64_t)t * qd + (uint64_t)h * HD + 16 * s + 4 * lq);
+    split4(q, qh[s], ql[s]);
   }
   f4v acc[NU];
 #pragma unroll
@@ -389,24 +400,29 @@ __global__ void __launch_bounds__(256) attention_mfma(float* Ao, const float* Qn
         kw = *(const uint4*)(K + (uint64_t)(k0 + key) * HD + c);
         vw = *(const uint4*)(V + (uint64_t)(k0 + key) * HD + c);
       }
-      const uint32_t kk[4] = {kw.x, kw.y, kw.z, kw.w}, vv[4] = {vw.x, vw.y, vw.z, vw.w};
+      uint2* kd = (uint2*)(Ks + key * KS + c);
+      kd[0] = make_uint2(kw.x, kw.y);
+      kd[1] = make_uint2(kw.z, kw.w);
+      const uint32_t vv[4] = {vw.x, vw.y, vw.z, vw.w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        Ks[key * KS + c + 2 * e] = h2f((uint16_t)(kk[e] & 0xFFFF));
-        Ks[key * KS + c + 2 * e + 1] = h2f((uint16_t)(kk[e] >> 16));
-        Vs[key * VS + c + 2 * e] = h2f((uint16_t)(vv[e] & 0xFFFF));
-        Vs[key * VS + c + 2 * e + 1] = h2f((uint16_t)(vv[e] >> 16));
+        Vt[(c + 2 * e) * VT + key] = (uint16_t)(vv[e] & 0xFFFF);
+        Vt[(c + 2 * e + 1) * VT + key] = (uint16_t)(vv[e] >> 16);
       }
     }
     __syncthreads();
-    // S = Q K^T for the 4 key tiles of 16
+    // S = Q K^T for the 4 key tiles of 16 (B operand: lane holds key
+    // 16 kt + lr, dims 16 s + 4 lq .. +3)
     f4v sc[4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
       sc[kt] = f4v{0.f, 0.f, 0.f, 0.f};
-      const float* kr = Ks + (kt * 16 + lr) * KS + lq;
 #pragma unroll
-      for (int s = 0; s < NS; ++s) sc[kt] = __builtin_amdgcn_mfma_f32_16x16x4f32(qf[s], kr[4 * s], sc[kt], 0, 0, 0);
+      for (int s = 0; s < NS; ++s) {
+        const h4v kb = *(const h4v*)(Ks + (kt * 16 + lr) * KS + 16 * s + 4 * lq);
+        sc[kt] = __builtin_amdgcn_mfma_f32_16x16x16f16(qh[s], kb, sc[kt], 0, 0, 0);
+        sc[kt] = __builtin_amdgcn_mfma_f32_16x16x16f16(ql[s], kb, sc[kt], 0, 0, 0);
+      }
     }
     // mask (key position > query position, or past the keys) and row maxima
     float bm[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
@@ -431,9 +447,9 @@ __global__ void __launch_bounds__(256) attention_mfma(float* Ao, const float* Qn
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float p = sc[kt][r] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sc[kt][r] - mn[r]);
-        rs[r] += p;
-        P[(4 * lq + r) * PS + kt * 16 + lr] = p;  // P[row][key]
+        const float pv = sc[kt][r] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sc[kt][r] - mn[r]);
+        rs[r] += pv;
+        P[(4 * lq + r) * PS + kt * 16 + lr] = pv;  // P[row][key]
       }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -447,13 +463,18 @@ __global__ void __launch_bounds__(256) attention_mfma(float* Ao, const float* Qn
     // the wave's own P tile: its LDS writes must land before its reads
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
     __builtin_amdgcn_wave_barrier();
-    // O += P V: A = P[row lr][key 4s + lq], B = V[key 4s + lq][dim 16u + lr]
-#pragma unroll 4
-    for (int s = 0; s < FK / 4; ++s) {
-      const float pa = P[lr * PS + 4 * s + lq];
-      const float* vr = Vs + (4 * s + lq) * VS + lr;
+    // O += P V: A = P[row lr][keys 16 s + 4 lq .. +3] (split into hi and lo),
+    // B = V[keys 16 s + 4 lq .. +3][dim 16 u + lr]
 #pragma unroll
-      for (int u = 0; u < NU; ++u) acc[u] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa, vr[16 * u], acc[u], 0, 0, 0);
+    for (int s = 0; s < FK / 16; ++s) {
+      h4v ph, pl;
+      split4(*(const float4*)(P + lr * PS + 16 * s + 4 * lq), ph, pl);
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        const h4v vb = *(const h4v*)(Vt + (16 * u + lr) * VT + 16 * s + 4 * lq);
+        acc[u] = __builtin_amdgcn_mfma_f32_16x16x16f16(ph, vb, acc[u], 0, 0, 0);
+        acc[u] = __builtin_amdgcn_mfma_f32_16x16x16f16(pl, vb, acc[u], 0, 0, 0);
+      }
     }
   }
   // O = acc / l, rows 4 lq + r, columns 16u + lr
