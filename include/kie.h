@@ -142,8 +142,10 @@ kie_status kie_prefill_scratch_bytes(const kie_ctx* ctx, int32_t chunk_tokens, s
  * monokernel runs prefill on the GPU (Kog explainer, "Monokernel" section);
  * batching the prompt reads every weight once per chunk of tokens instead
  * of once per token.  All prompt tokens but the last go through batched
- * GEMMs (fp32 activations, fp16 weights, fp32 accumulation), RoPE, fp16 KV
- * append and causal attention, chunk by chunk; the last one runs through
+ * GEMMs (fp32 activations, fp16 weights, fp32 accumulation; on the fp16
+ * matrix cores, each activation entering as an fp16 hi + lo pair, so the
+ * products keep fp32 accuracy to ~2^-22), RoPE, fp16 KV append and causal
+ * attention (likewise), chunk by chunk; the last one runs through
  * the decode kernel, which yields t1 (greedy or sampled, see
  * kie_set_sampling).  d_scratch is caller-owned device memory (16-byte
  * aligned) of scratch_bytes; the chunk is the largest that fits, at most
