@@ -83,18 +83,18 @@ __global__ void __launch_bounds__(kRowThreads) rmsnorm(float* Y, int ldy, const 
 // Out[m][n] (+)= sum_k A[m][k] * W[n][k] for m < M, n < N.  W is a packed
 // matrix: row pairs, each cut into 256-column blocks of one 1 KB chunk (256
 // columns of row 2p, then the same columns of row 2p+1, zero past K).
-// Tile 64 (m) x 128 (n) x 32 (k) per workgroup of 4 waves; wave w owns
+// Tile 64 (m) x 128 (n) x 64 (k) per workgroup of 4 waves; wave w owns
 // columns n0 + 32w .. +32 and both 32-row halves, two 32x32 accumulators.
 // The next k tile is fetched into registers while the current one is
 // multiplied from LDS (double-buffered).
-constexpr int BM = 64, BN = 128, BK = 32;
+constexpr int BM = 64, BN = 128, BK = 64;
 
 // The product runs on the fp16 matrix cores to fp32 accuracy: each fp32
 // activation a is split into hi = fp16(a) and lo = fp16(a - hi), so that
 // hi + lo = a to about 2^-22 relative, and the weights are fp16 already;
 // hi * W and lo * W accumulate in fp32 (v_mfma_f32_32x32x8f16, two per
 // k-step of 8).  The split happens once, when a tile is staged in LDS.  LDS
-// rows hold 36 halves (72 bytes), so that the 32 rows a fragment read
+// rows hold 68 halves (136 bytes), so that the 32 rows a fragment read
 // touches start in different banks.
 constexpr int HP = BK + 4;
 
@@ -108,15 +108,17 @@ __global__ void __launch_bounds__(256) gemm16(float* Out, int ldo, const float* 
   const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
   const int nkt = (K + BK - 1) / BK;
   const int cb = col_blocks(K);
+  // loads of this thread: A rows ar and ar + 32, columns ak + 32 c .. +3
+  // (c < 2); B row bn (packed), columns bk .. bk + 31
   const int ar = tid >> 3, ak = (tid & 7) * 4;
-  const int bn = tid >> 1, bk = (tid & 1) * 16;
-  float4 ra[2];
-  uint4 rb[2];
+  const int bn = tid >> 1, bk = (tid & 1) * 32;
+  float4 ra[4];
+  uint4 rb[4];
   auto fetch = [&](int kt) {
     const int k0 = kt * BK;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int m = m0 + ar + 32 * h, k = k0 + ak;
+    for (int h = 0; h < 4; ++h) {
+      const int m = m0 + ar + 32 * (h & 1), k = k0 + ak + 32 * (h >> 1);
       float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
       if (m < M) {
         const float* a = A + (uint64_t)m * lda + k;
@@ -131,29 +133,30 @@ __global__ void __launch_bounds__(256) gemm16(float* Out, int ldo, const float* 
       }
       ra[h] = v;
     }
-    const int n = n0 + bn, k = k0 + bk;  // k + 15 < 256 * cb: the padded row holds it
+    const int n = n0 + bn, k = k0 + bk;  // k + 31 < 256 * cb: the padded row holds it
     if (n < N) {
       const uint16_t* w = Wm + ((uint64_t)(n >> 1) * cb + (k >> 8)) * 512 + (n & 1) * 256 + (k & 255);
-      rb[0] = *(const uint4*)w;
-      rb[1] = *(const uint4*)(w + 8);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) rb[i] = *(const uint4*)(w + 8 * i);
     } else {
-      rb[0] = make_uint4(0, 0, 0, 0);
-      rb[1] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) rb[i] = make_uint4(0, 0, 0, 0);
     }
   };
   auto stash = [&](int buf) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < 4; ++h) {
       h4v hi, lo;
       split4(ra[h], hi, lo);
-      *(h4v*)&Ah[buf][ar + 32 * h][ak] = hi;
-      *(h4v*)&Al[buf][ar + 32 * h][ak] = lo;
+      *(h4v*)&Ah[buf][ar + 32 * (h & 1)][ak + 32 * (h >> 1)] = hi;
+      *(h4v*)&Al[buf][ar + 32 * (h & 1)][ak + 32 * (h >> 1)] = lo;
     }
     uint2* d = (uint2*)&Bh[buf][bn][bk];
-    d[0] = make_uint2(rb[0].x, rb[0].y);
-    d[1] = make_uint2(rb[0].z, rb[0].w);
-    d[2] = make_uint2(rb[1].x, rb[1].y);
-    d[3] = make_uint2(rb[1].z, rb[1].w);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      d[2 * i] = make_uint2(rb[i].x, rb[i].y);
+      d[2 * i + 1] = make_uint2(rb[i].z, rb[i].w);
+    }
   };
   f16v acc[2];
 #pragma unroll
