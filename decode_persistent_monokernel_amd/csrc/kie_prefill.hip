@@ -92,11 +92,12 @@ constexpr int BM = 64, BN = 128, BK = 64;
 // The product runs on the fp16 matrix cores to fp32 accuracy: each fp32
 // activation a is split into hi = fp16(a) and lo = fp16(a - hi), so that
 // hi + lo = a to about 2^-22 relative, and the weights are fp16 already;
-// hi * W and lo * W accumulate in fp32 (v_mfma_f32_32x32x8f16, two per
-// k-step of 8).  The split happens once, when a tile is staged in LDS.  LDS
-// rows hold 68 halves (136 bytes), so that the 32 rows a fragment read
-// touches start in different banks.
-constexpr int HP = BK + 4;
+// hi * W and lo * W accumulate in fp32 (v_mfma_f32_32x32x16_f16, two per
+// k-step of 16, operands read from LDS 16 bytes per lane).  The split happens
+// once, when a tile is staged in LDS.  LDS rows hold 72 halves (144 bytes, a
+// multiple of 16 for the 16-byte reads).
+typedef _Float16 h8v __attribute__((ext_vector_type(8)));
+constexpr int HP = BK + 8;
 
 template <bool ADD>
 __global__ void __launch_bounds__(256) gemm16(float* Out, int ldo, const float* A, int lda, const uint16_t* Wm,
@@ -171,16 +172,16 @@ __global__ void __launch_bounds__(256) gemm16(float* Out, int ldo, const float* 
     const int buf = kt & 1;
     if (kt + 1 < nkt) fetch(kt + 1);
 #pragma unroll
-    for (int kk = 0; kk < BK; kk += 8) {
-      // operands: lane l holds row (or column) l % 32, k = kk + 4 (l / 32) .. +3
-      const int kq = kk + 4 * lk;
-      const h4v b = *(const h4v*)&Bh[buf][wave * 32 + li][kq];
+    for (int kk = 0; kk < BK; kk += 16) {
+      // operands: lane l holds row (or column) l % 32, k = kk + 8 (l / 32) .. +7
+      const int kq = kk + 8 * lk;
+      const h8v b = *(const h8v*)&Bh[buf][wave * 32 + li][kq];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        const h4v ah = *(const h4v*)&Ah[buf][32 * i + li][kq];
-        const h4v al = *(const h4v*)&Al[buf][32 * i + li][kq];
-        acc[i] = __builtin_amdgcn_mfma_f32_32x32x8f16(ah, b, acc[i], 0, 0, 0);
-        acc[i] = __builtin_amdgcn_mfma_f32_32x32x8f16(al, b, acc[i], 0, 0, 0);
+        const h8v ah = *(const h8v*)&Ah[buf][32 * i + li][kq];
+        const h8v al = *(const h8v*)&Al[buf][32 * i + li][kq];
+        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, b, acc[i], 0, 0, 0);
+        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, b, acc[i], 0, 0, 0);
       }
     }
     if (kt + 1 < nkt) stash(buf ^ 1);
