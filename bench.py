@@ -111,7 +111,7 @@ def summarize_trace(d: str, command: str) -> str:
     title = ("# rocprofv3 kernel trace of the batched prefill benchmark (cfg2, 2048-token prompt, chunks of 1024)"
              if prefill else
              "# rocprofv3 kernel trace of the default benchmark run (cfg2, 2048-token prompt, 512 decode steps)")
-    out = [title, "", "Command (from the repository root on the GPU box):", "", "```", command, "```", "",
+    out = [title, "", "Command (from the repository root, on an MI355X):", "", "```", command, "```", "",
            "| kernel | calls | total ms | average ms | min ms | max ms |", "|---|---|---|---|---|---|"]
     for r in stats:
         ns = lambda k: float(r[k]) / 1e6
@@ -205,8 +205,8 @@ def main():
         return
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
-              "multi-GPU decode is not part of it", file=sys.stderr)
+        print(f"bench.py: decode runs on one GPU only (asked for --gpus {args.gpus}); "
+              "multi-GPU decode is not implemented", file=sys.stderr)
         sys.exit(2)
 
     import torch
