@@ -1071,6 +1071,40 @@ KIE_DI void rmsnorm_to_xs2(const Dev& D, const float* xraw, const uint16_t (&ga)
   }
 }
 
+// The sequential block's RMSNorm with the scale left to the epilogue:
+// W (g * x / rms) = (W (g * x)) / rms, so the prologue writes g * x and each
+// wave's sum of squares (to redf), and the epilogue, after the barrier it
+// has anyway, multiplies the outputs by rms_inv.  No barrier or second pass
+// sits between the input and the stream.
+KIE_DI void gain_to_xs(const Dev& D, const float* xraw, const uint16_t (&gr)[kGainRegs], float* xs) {
+  const int d = D.p->m.d;
+  const int t = opaque(D.tid);
+  float xv[kGainRegs];
+#pragma unroll
+  for (int k = 0; k < kGainRegs; ++k) {
+    const int i = t + k * kThreads;
+    xv[k] = xraw[i < d ? i : 0];
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int k = 0; k < kGainRegs; ++k) ss += t + k * kThreads < d ? xv[k] * xv[k] : 0.f;
+  ss = wave_sum(ss);
+  if (D.lane == 0) D.sh->redf[D.wave] = ss;
+  const int padded = padded_cols(d);
+#pragma unroll
+  for (int k = 0; k < kGainRegs; ++k) {
+    const int i = t + k * kThreads;
+    if (i < padded) xs[xs_pos(i, D.plane)] = i < d ? xv[k] * hbits2f(gr[k]) : 0.f;
+  }
+}
+// 1 / sqrt(mean(x^2) + eps) from the waves' sums (after a barrier)
+KIE_DI float rms_inv(const Dev& D) {
+  float tot = 0.f;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) tot += D.sh->redf[w];
+  return 1.0f / sqrtf(tot / (float)D.p->m.d + D.p->m.eps);
+}
+
 // the zero columns of a padded row (padded_cols(K) > K)
 KIE_DI void zero_tail(const Dev& D, float* xs, int K) {
   const int padded = padded_cols(K);
@@ -1544,7 +1578,11 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
           }
           rmsnorm_to_xs2(D, xraw, gr, xs, gg, hbs);
         } else {
-          rmsnorm_to_xs(D, xraw, gr, xs);
+          if (PAR) {
+            rmsnorm_to_xs(D, xraw, gr, xs);
+          } else {
+            gain_to_xs(D, xraw, gr, xs);
+          }
         }
       } else if (kind == PH_GU && early) {
         // input prepared by the QKV prologue
@@ -1559,7 +1597,11 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
           wg_sync();
           if (aborted(D)) { __builtin_amdgcn_s_waitcnt(kWaitAllVm); return; }
         }
-        rmsnorm_to_xs(D, xraw, gr, xs);
+        if (PAR) {
+          rmsnorm_to_xs(D, xraw, gr, xs);
+        } else {
+          gain_to_xs(D, xraw, gr, xs);
+        }
       } else if (kind == PH_O) {
         if (early) {
           const bool next = l + 1 < L;
@@ -1613,7 +1655,11 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
         poll_to_lds<false>(D, D.X + (uint64_t)(2 * L) * d, xraw, d, epoch);
         wg_sync();
         if (aborted(D)) { __builtin_amdgcn_s_waitcnt(kWaitAllVm); return; }
-        rmsnorm_to_xs(D, xraw, gr, xs);
+        if (PAR) {
+          rmsnorm_to_xs(D, xraw, gr, xs);
+        } else {
+          gain_to_xs(D, xraw, gr, xs);
+        }
       }
       for (int i = D.tid; i < nrows * kWaves; i += kThreads) part[i] = 0.f;
       wg_sync();
@@ -1629,6 +1675,8 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
       wg_sync();
 
       // epilogue
+      // the sequential block's deferred RMSNorm scale (gain_to_xs)
+      const float ninv = (!PAR && (kind == PH_QKV || kind == PH_GU || kind == PH_LM)) ? rms_inv(D) : 1.f;
       if (kind == PH_QKV) {
         const float qscale = 1.4426950408889634f / sqrtf((float)hd);
         const float2* rp = D.rope + (uint64_t)pos * (hd / 2);
@@ -1639,6 +1687,8 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
             y0 += part[(2 * t) * kWaves + w];
             y1 += part[(2 * t + 1) * kWaves + w];
           }
+          y0 *= ninv;
+          y1 *= ninv;
           const int rr = r0 + 2 * t;
           if (rr < qd + kvd) {
             const bool isq = rr < qd;
@@ -1681,6 +1731,8 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
             y0 += part[(2 * t) * kWaves + w];
             y1 += part[(2 * t + 1) * kWaves + w];
           }
+          y0 *= ninv;
+          y1 *= ninv;
           const float hval = y0 / (1.0f + expf(-y0)) * y1;
           ll_storef(D.HB + (uint64_t)l * F + (r0 >> 1) + t, hval, epoch);
         }
@@ -1723,6 +1775,7 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
           float y = 0.f;
 #pragma unroll
           for (int w = 0; w < kWaves; ++w) y += part[t * kWaves + w];
+          y *= ninv;
           const int row = r0 + t;
           if (p.logits) p.logits[(uint64_t)out_step * V + row] = y;
           // sampling: the Gumbel-max draw over logits / T
