@@ -1036,42 +1036,7 @@ KIE_DI void rmsnorm_to_xs(const Dev& D, const float* xraw, const uint16_t (&gr)[
   }
 }
 
-// the same normalisation for two gain vectors at once (the parallel block's
-// QKV and gate/up read the same x_l): xa with gains ga, xb with gains gb
-KIE_DI void rmsnorm_to_xs2(const Dev& D, const float* xraw, const uint16_t (&ga)[kGainRegs], float* xa,
-                           const uint16_t (&gb)[kGainRegs], float* xb) {
-  const KParams& p = *D.p;
-  const int d = p.m.d;
-  const int t = opaque(D.tid);
-  float xv[kGainRegs];
-#pragma unroll
-  for (int k = 0; k < kGainRegs; ++k) {
-    const int i = t + k * kThreads;
-    xv[k] = xraw[i < d ? i : 0];
-  }
-  float ss = 0.f;
-#pragma unroll
-  for (int k = 0; k < kGainRegs; ++k) ss += t + k * kThreads < d ? xv[k] * xv[k] : 0.f;
-  ss = wave_sum(ss);
-  if (D.lane == 0) D.sh->redf[D.wave] = ss;
-  wg_sync();
-  float tot = 0.f;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) tot += D.sh->redf[w];
-  const float inv = 1.0f / sqrtf(tot / (float)d + p.m.eps);
-  const int padded = padded_cols(d);
-#pragma unroll
-  for (int k = 0; k < kGainRegs; ++k) {
-    const int i = t + k * kThreads;
-    if (i < padded) {
-      const float xn = xv[k] * inv;
-      xa[xs_pos(i, D.plane)] = i < d ? xn * hbits2f(ga[k]) : 0.f;
-      xb[xs_pos(i, D.plane)] = i < d ? xn * hbits2f(gb[k]) : 0.f;
-    }
-  }
-}
-
-// The sequential block's RMSNorm with the scale left to the epilogue:
+// RMSNorm with the scale left to the epilogue:
 // W (g * x / rms) = (W (g * x)) / rms, so the prologue writes g * x and each
 // wave's sum of squares (to redf), and the epilogue, after the barrier it
 // has anyway, multiplies the outputs by rms_inv.  No barrier or second pass
@@ -1104,6 +1069,35 @@ KIE_DI float rms_inv(const Dev& D) {
   for (int w = 0; w < kWaves; ++w) tot += D.sh->redf[w];
   return 1.0f / sqrtf(tot / (float)D.p->m.d + D.p->m.eps);
 }
+
+// the same for two gain vectors at once (the parallel block's QKV and
+// gate/up read the same x_l): xa = ga * x, xb = gb * x, scale deferred
+KIE_DI void gain2_to_xs(const Dev& D, const float* xraw, const uint16_t (&ga)[kGainRegs], float* xa,
+                        const uint16_t (&gb)[kGainRegs], float* xb) {
+  const int d = D.p->m.d;
+  const int t = opaque(D.tid);
+  float xv[kGainRegs];
+#pragma unroll
+  for (int k = 0; k < kGainRegs; ++k) {
+    const int i = t + k * kThreads;
+    xv[k] = xraw[i < d ? i : 0];
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int k = 0; k < kGainRegs; ++k) ss += t + k * kThreads < d ? xv[k] * xv[k] : 0.f;
+  ss = wave_sum(ss);
+  if (D.lane == 0) D.sh->redf[D.wave] = ss;
+  const int padded = padded_cols(d);
+#pragma unroll
+  for (int k = 0; k < kGainRegs; ++k) {
+    const int i = t + k * kThreads;
+    if (i < padded) {
+      xa[xs_pos(i, D.plane)] = i < d ? xv[k] * hbits2f(ga[k]) : 0.f;
+      xb[xs_pos(i, D.plane)] = i < d ? xv[k] * hbits2f(gb[k]) : 0.f;
+    }
+  }
+}
+
 
 // the zero columns of a padded row (padded_cols(K) > K)
 KIE_DI void zero_tail(const Dev& D, float* xs, int K) {
@@ -1576,7 +1570,7 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
           } else {
             load_gains(D, Wl + p.pl.mlp_norm, gg);
           }
-          rmsnorm_to_xs2(D, xraw, gr, xs, gg, hbs);
+          gain2_to_xs(D, xraw, gr, xs, gg, hbs);
         } else {
           if (PAR) {
             rmsnorm_to_xs(D, xraw, gr, xs);
@@ -1655,11 +1649,7 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
         poll_to_lds<false>(D, D.X + (uint64_t)(2 * L) * d, xraw, d, epoch);
         wg_sync();
         if (aborted(D)) { __builtin_amdgcn_s_waitcnt(kWaitAllVm); return; }
-        if (PAR) {
-          rmsnorm_to_xs(D, xraw, gr, xs);
-        } else {
-          gain_to_xs(D, xraw, gr, xs);
-        }
+        gain_to_xs(D, xraw, gr, xs);
       }
       for (int i = D.tid; i < nrows * kWaves; i += kThreads) part[i] = 0.f;
       wg_sync();
@@ -1675,8 +1665,10 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
       wg_sync();
 
       // epilogue
-      // the sequential block's deferred RMSNorm scale (gain_to_xs)
-      const float ninv = (!PAR && (kind == PH_QKV || kind == PH_GU || kind == PH_LM)) ? rms_inv(D) : 1.f;
+      // the deferred RMSNorm scale (gain_to_xs / gain2_to_xs); the parallel
+      // block's gate/up reads the sums its QKV prologue left
+      const bool deferred = kind == PH_LM || ((kind == PH_QKV || kind == PH_GU) && (!PAR || early));
+      const float ninv = deferred ? rms_inv(D) : 1.f;
       if (kind == PH_QKV) {
         const float qscale = 1.4426950408889634f / sqrtf((float)hd);
         const float2* rp = D.rope + (uint64_t)pos * (hd / 2);
