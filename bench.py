@@ -108,7 +108,7 @@ def summarize_trace(d: str, command: str) -> str:
     stats = _rows(d, "kernel_stats.csv")
     trace = _rows(d, "kernel_trace.csv")
     prefill = "--prefill" in command
-    title = ("# rocprofv3 kernel trace of the batched prefill benchmark (cfg2, 2048-token prompt, chunks of 1024)"
+    title = ("# rocprofv3 kernel trace of the batched prefill benchmark (cfg2, 2048-token prompt, chunks of 2048)"
              if prefill else
              "# rocprofv3 kernel trace of the default benchmark run (cfg2, 2048-token prompt, 512 decode steps)")
     out = [title, "", "Command (from the repository root, on an MI355X):", "", "```", command, "```", "",
@@ -340,7 +340,7 @@ def prefill_bench(args, cfg, eng, prompt):
     dev = eng.dev
     d_prompt = torch.tensor(np.asarray(prompt, dtype=np.int32), device=dev)
     d_next = torch.empty(1, dtype=torch.int32, device=dev)
-    chunk = 1024
+    chunk = 2048
     scratch = torch.empty(eng.prefill_scratch_bytes(chunk) // 4, dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
     times = []

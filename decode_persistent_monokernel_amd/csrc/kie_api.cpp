@@ -46,7 +46,7 @@ struct kie_ctx {
 
 namespace {
 
-constexpr int32_t kPrefillChunk = 1024;  // most prompt tokens per batched-prefill chunk
+constexpr int32_t kPrefillChunk = 2048;  // most prompt tokens per batched-prefill chunk
 
 kie_status fail(kie_ctx* c, kie_status s, const std::string& msg) {
   if (c) c->err = msg;

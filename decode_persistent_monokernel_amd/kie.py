@@ -301,7 +301,7 @@ class Engine:
                                           scratch.data_ptr(), scratch.numel() * scratch.element_size(),
                                           self.stream()), self.ctx)
 
-    def prefill_batched(self, prompt: Sequence[int], want_logits: bool = False, chunk: int = 1024):
+    def prefill_batched(self, prompt: Sequence[int], want_logits: bool = False, chunk: int = 2048):
         """kie_prefill_batched with a scratch buffer for `chunk` tokens"""
         t = self.torch
         d_prompt = self._ids(prompt)

@@ -149,7 +149,7 @@ kie_status kie_prefill_scratch_bytes(const kie_ctx* ctx, int32_t chunk_tokens, s
  * the decode kernel, which yields t1 (greedy or sampled, see
  * kie_set_sampling).  d_scratch is caller-owned device memory (16-byte
  * aligned) of scratch_bytes; the chunk is the largest that fits, at most
- * 1024 tokens (kie_prefill_scratch_bytes gives the size for a chunk).  The
+ * 2048 tokens (kie_prefill_scratch_bytes gives the size for a chunk).  The
  * lane-structured block keeps its delayed residual (layer l reads
  * x_0 + P_0 + .. + P_{l-delay-1}).  ffn_dim not a multiple of 4 and a
  * one-token prompt fall back to kie_prefill.  KIE_ERR_INVALID_ARG if the
