@@ -168,6 +168,99 @@ def summarize_traffic(fetch_dir: str, write_dir: str, copy_bytes: int, cfg_name:
     }
 
 
+# ---------------------------------------------------------------------------
+# per-phase critical path from the kernel's own wall-clock stamps
+# ---------------------------------------------------------------------------
+PHASE_NAMES_SEQ = ("QKV", "attention", "O", "gate/up", "down")
+PHASE_NAMES_PAR = ("QKV", "gate/up", "attention", "O", "down")
+END_PHASE = 5 * 64 + 1
+
+
+def phase_trace_summary(tr: np.ndarray, cfg, untraced_ms_per_token: float, command: str) -> str:
+    """Markdown attribution of one token's time from kie_set_trace stamps
+    tr[step, phase, workgroup, 4] (100 MHz ticks: phase start, input ready,
+    stream done, phase end; attention: start, query ready, records stored,
+    end after the merge).
+
+    Critical path: for every phase, `hop` is the time from the previous
+    phase's last end to this phase's last input-ready stamp (the dependency
+    exchange the slowest consumer waited for), `work` from that to this
+    phase's last end (its stream and epilogue).  The end of a step (release,
+    token gather, acquire) follows the LM head.  Per workgroup: the share of
+    its time spent between a phase's start and its input being ready (waiting
+    on other workgroups), the analogue of a grid-synchronisation share."""
+    tick_us = 0.01
+    L = cfg.n_layers
+    names = PHASE_NAMES_SEQ if cfg.sequential else PHASE_NAMES_PAR
+    steps = list(range(1, tr.shape[0]))  # the launch's first step also fills the ring: left out
+    phases = list(range(5 * L)) + [5 * L]
+    hop = {n: [] for n in names + ("LM head",)}
+    work = {n: [] for n in names + ("LM head",)}
+    wait_share, tok_us, end_us, first_hop = [], [], [], []
+    per_phase_wait = {n: [] for n in names + ("LM head",)}
+    for s in steps:
+        t = tr[s].astype(np.float64)
+        start = t[0, :, 0].min()
+        prev_end = start
+        waited = np.zeros(tr.shape[2])
+        for ph in phases:
+            nm = "LM head" if ph == 5 * L else names[ph % 5]
+            st = t[ph]
+            r_max, e_max = st[:, 1].max(), st[:, 3].max()
+            hop[nm].append((r_max - prev_end) * tick_us)
+            work[nm].append((e_max - r_max) * tick_us)
+            w = st[:, 1] - st[:, 0]
+            waited += w
+            per_phase_wait[nm].append(w.mean() * tick_us)
+            prev_end = e_max
+        e = t[END_PHASE]
+        step_end = e[:, 1].max()
+        end_us.append((step_end - prev_end) * tick_us)
+        nxt = tr[s + 1][0, :, 0].min() if s + 1 < tr.shape[0] else None
+        total = ((nxt if nxt is not None else step_end) - start) * tick_us
+        tok_us.append(total)
+        wait_share.append(float(np.mean(waited * tick_us / total)))
+    T = float(np.mean(tok_us))
+    out = [f"# Per-phase critical path of one decode token ({cfg.name}, {cfg.n_layers} layers)", "",
+           "From the kernel's own phase stamps (`kie_set_trace`, wall clock at 100 MHz) over "
+           f"{len(steps)} decode steps; the stamps are kept in LDS and written out at the end of each step.", "",
+           "Command (from the repository root, on an MI355X):", "", "```", command, "```", "",
+           f"- traced token time: {T:.1f} us (untraced, same run: {untraced_ms_per_token * 1e3:.1f} us)",
+           f"- per layer: {T / L:.2f} us",
+           f"- share of a workgroup's time spent waiting for another workgroup's output (phase start to input "
+           f"ready, summed over phases, mean over workgroups): **{100 * np.mean(wait_share):.1f} %**", "",
+           "Critical path per token (sum over the layers of the phase; `hop` = previous phase's last end to "
+           "this phase's last input ready, `work` = that to this phase's last end):", "",
+           "| phase | hop us/token | work us/token | hop+work | share of token | mean wait per workgroup us/token |",
+           "|---|---|---|---|---|---|"]
+    nsteps = len(steps)
+    tot_hop = tot_work = 0.0
+    for nm in names + ("LM head",):
+        h = sum(hop[nm]) / nsteps
+        w = sum(work[nm]) / nsteps
+        pw = sum(per_phase_wait[nm]) / nsteps
+        tot_hop += h
+        tot_work += w
+        out.append(f"| {nm} | {h:.1f} | {w:.1f} | {h + w:.1f} | {100 * (h + w) / T:.1f} % | {pw:.1f} |")
+    E = float(np.mean(end_us))
+    out.append(f"| end of step (release, token gather, acquire) | {E:.1f} | - | {E:.1f} | {100 * E / T:.1f} % | - |")
+    out += ["", f"Hops total {tot_hop + E:.1f} us/token ({100 * (tot_hop + E) / T:.1f} % of the token); "
+            f"work total {tot_work:.1f} us/token ({100 * tot_work / T:.1f} %)."]
+    return "\n".join(out) + "\n"
+
+
+def release_engine(eng) -> None:
+    """destroy the library context, then free the engine's device tensors and
+    hand the cached blocks back to the runtime"""
+    import torch
+    eng.close()
+    for name in ("d_packed", "d_kv", "d_ws", "_trace"):
+        if hasattr(eng, name):
+            setattr(eng, name, None)
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -187,6 +280,12 @@ def main():
                     help="print the JSON traffic summary of two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) "
                          "of this command with --copy-bytes and exit")
     ap.add_argument("--command", default="", help="the profiled command, recorded in a summary")
+    ap.add_argument("--launch-steps", type=int, default=0,
+                    help="decode steps per kernel launch (default: all timed steps in one launch); 1 measures the "
+                         "per-token launch cost the persistent kernel removes")
+    ap.add_argument("--phase-trace", metavar="FILE", default="",
+                    help="after the timed run, trace 16 decode steps and write the per-phase critical-path "
+                         "summary (markdown) to FILE")
     ap.add_argument("--prefill", action="store_true",
                     help="instead of the decode benchmark, time the batched prefill of the prompt and print "
                          "its own JSON line (matrix-core roofline)")
@@ -222,7 +321,8 @@ def main():
     w = gen_weights(cfg)
     prompt = gen_prompt(cfg, n=P)
     eng = Engine(cfg, device=0, max_ctx=max_ctx)
-    eng.set_launch_steps(max(K, W, 1))
+    per_launch = args.launch_steps if args.launch_steps > 0 else max(K, W, 1)
+    eng.set_launch_steps(per_launch)
     eng.load_weights(w)
     if args.prefill:
         prefill_bench(args, cfg, eng, prompt)
@@ -264,7 +364,7 @@ def main():
         launch_ms.append(a.elapsed_time(b))
         eng.sync()
 
-    n_launches = (K + max(K, W, 1) - 1) // max(K, W, 1)
+    n_launches = (K + per_launch - 1) // per_launch
     algo_bytes = cfg.run_bytes(P, K)
     achieved = algo_bytes / (kernel_ms * 1e-3) / 1e9
     traffic = measured_traffic(cfg.name, P, K)
@@ -305,7 +405,23 @@ def main():
         },
         "tokens_head": [int(t) for t in toks[:8]],
     }
-    eng.close()
+    if args.phase_trace:
+        # 16 traced steps from the same position (a separate launch, after
+        # the timed one)
+        eng.set_position(P, t1)
+        eng.set_launch_steps(16)
+        eng.set_trace(16)
+        eng.decode_device(16, out)
+        eng.sync()
+        tr = eng.trace()
+        eng.set_trace(0)
+        cmd = "python bench.py " + " ".join(a for a in sys.argv[1:])
+        with open(args.phase_trace, "w") as fh:
+            fh.write(phase_trace_summary(tr, cfg, wall * 1e3 / K, cmd))
+    # release every device buffer while the runtime (and a profiler attached
+    # to it) is still fully up: nothing is left for interpreter teardown
+    del out
+    release_engine(eng)
     del eng
     if args.copy_bytes > 0:
         src = torch.ones(args.copy_bytes // 4, dtype=torch.float32, device=dev)
@@ -314,6 +430,7 @@ def main():
         torch.mul(src, 1.0, out=dst)  # an elementwise kernel: reads and writes copy_bytes
         torch.cuda.synchronize()
         del src, dst
+        torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, w, P, args.cpu_steps)
     print(json.dumps(res), flush=True)
@@ -377,7 +494,8 @@ def prefill_bench(args, cfg, eng, prompt):
                      "flops": flops, "all_ms": [round(x, 3) for x in times]},
         "next_token": int(d_next.cpu()[0]),
     }
-    eng.close()
+    del d_prompt, d_next, scratch
+    release_engine(eng)
     print(json.dumps(res), flush=True)
 
 

@@ -465,6 +465,8 @@ kie_status kie_sync_status(kie_ctx* c, void* stream) {
   if (e != hipSuccess) return hip_fail(c, e, "reset exchange state");
   c->next_epoch = 1;
   if (st[0] == kie::DEV_BAD_TOKEN) return fail(c, KIE_ERR_BAD_TOKEN, "a token id outside [0, vocab) reached the kernel");
+  if (st[0] == kie::DEV_RANGE)
+    return fail(c, KIE_ERR_RANGE, "a prefill activation outside the fp16 range (|a| > 65504 or not finite)");
   return fail(c, KIE_ERR_TIMEOUT, "a wait inside the decode kernel timed out");
 }
 
@@ -630,6 +632,7 @@ const char* kie_status_string(kie_status s) {
     case KIE_ERR_TIMEOUT: return "wait timed out inside the kernel";
     case KIE_ERR_UNSUPPORTED: return "unsupported model shape";
     case KIE_ERR_BAD_TOKEN: return "token id out of range";
+    case KIE_ERR_RANGE: return "prefill activation outside the fp16 range";
   }
   return "unknown status";
 }

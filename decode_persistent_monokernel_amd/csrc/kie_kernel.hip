@@ -276,6 +276,21 @@ KIE_DI bool spin_word(const Dev& D, const u64* a, uint32_t epoch, u64* out) {
   }
 }
 
+// Race-detection aid (DBG_JITTER): each wave sleeps a pseudo-random time,
+// 0 to ~6 us, at the start of every phase, hashed from (workgroup, wave,
+// epoch, phase), so every launch reorders the workgroups' arrivals.  Results
+// must not change by a single bit: each output has one owner and a fixed
+// order of additions.
+KIE_DI void jitter(const Dev& D, uint32_t epoch, int ph) {
+  uint32_t h = (uint32_t)D.wg * 0x9E3779B1u ^ (uint32_t)D.wave * 0x85EBCA77u ^ epoch * 0xC2B2AE3Du ^
+               (uint32_t)ph * 0x27D4EB2Fu;
+  h ^= h >> 15;
+  h *= 0x2C1B3C6Du;
+  h ^= h >> 12;
+  const int n = rfl((int)(h & 15));
+  for (int i = 0; i < n; ++i) __builtin_amdgcn_s_sleep(16);
+}
+
 // Phase trace stamp (thread 0 of the workgroup only).  Stamps go to LDS and
 // reach memory at the end of the step: a global store here would be waited
 // for by the next vmcnt wait of the wave and move the very times measured.
@@ -1285,6 +1300,7 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
       const uint16_t* Wl = p.W + (uint64_t)(is_lm ? 0 : l) * p.pl.layer_stride;
 
       stamp(D, s, ph, 0);
+      if (p.debug_flags & DBG_JITTER) jitter(D, epoch, ph);
       if (kind == PH_ATTN) {
         // ================= attention over the KV cache ==================
         float mrow[G], lrow[G], acc[G][8], q[G][8];
@@ -1322,6 +1338,7 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
         }
         wg_sync();
         if (aborted(D)) { __builtin_amdgcn_s_waitcnt(kWaitAllVm); return; }
+        stamp(D, s, ph, 1);
         for (int sg = 0; sg < nseg; ++sg) {
           const int ka = rfl(adesc[5 * sg + 1]), kc = rfl(adesc[5 * sg + 2]), nst = rfl(adesc[5 * sg + 3]);
           const int has_pos = rfl(adesc[5 * sg + 4]);
@@ -1389,7 +1406,6 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
             }
           }
         }
-        stamp(D, s, ph, 1);
         wg_sync();
         if (aborted(D)) { __builtin_amdgcn_s_waitcnt(kWaitAllVm); return; }
         // workgroup merge of the waves -> one record per segment
@@ -1792,6 +1808,7 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
     const int tph = 5 * 64 + 1;
     stamp(D, s, tph, 0);
     const bool lm = lm_active(p, s);
+    if (p.debug_flags & DBG_JITTER) jitter(D, epoch, tph);
     // every thread's KV-cache stores have reached the L2 before thread 0's
     // release fence writes the L2 back (one write-back per workgroup)
     __builtin_amdgcn_s_waitcnt(kWaitAllVm);

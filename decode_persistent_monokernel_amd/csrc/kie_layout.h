@@ -428,7 +428,7 @@ struct PrefillArgs {
   const uint16_t* W;     // packed weights
   uint16_t* kv;          // KV cache
   const float2* rope;    // [max_ctx][hd/2] (cos, sin)
-  int32_t* state;        // device status words (bad token -> DEV_BAD_TOKEN)
+  int32_t* state;        // device status words (bad token -> DEV_BAD_TOKEN, fp16 range -> DEV_RANGE)
   const int32_t* tokens; // [C] device ids of this chunk
   int C, pos0;
   float* scratch;
@@ -448,8 +448,9 @@ KIE_HD uint64_t pf_floats_per_token(const Dims& m) {
 
 enum DebugFlags : uint32_t {
   DBG_WAIT_NEVER = 1u,  // workgroup 0 waits on a word no one writes (timeout test)
+  DBG_JITTER = 2u,      // every wave sleeps a pseudo-random time at every phase start
 };
 
-enum DeviceStatus : int32_t { DEV_OK = 0, DEV_TIMEOUT = 1, DEV_BAD_TOKEN = 2 };
+enum DeviceStatus : int32_t { DEV_OK = 0, DEV_TIMEOUT = 1, DEV_BAD_TOKEN = 2, DEV_RANGE = 3 };
 
 }  // namespace kie

@@ -29,15 +29,21 @@ constexpr int kRowThreads = 256;
 
 __device__ __forceinline__ float h2f(uint16_t u) { return __half2float(__ushort_as_half(u)); }
 
-// fp32 values as fp16 pairs for the fp16 matrix cores: hi = fp16(x),
-// lo = fp16(x - hi), hi + lo = x to about 2^-22 relative
+// fp32 values as fp16 pairs for the fp16 matrix cores: hi = fp16(x) and
+// lo = fp16((x - hi) * 2^11), so that x = hi + lo * 2^-11 to about 2^-22
+// relative.  The remainder x - hi is scaled by the power of two 2^11 (exact)
+// before its rounding: unscaled it falls below fp16's normal range whenever
+// |x| < 2^-3, and the matrix cores would see a subnormal (or flushed)
+// operand.  Products of lo go to their own fp32 accumulator, which is scaled
+// back by 2^-11 once, at the end.  Both parts stay normal for |x| >= 2^-14.
 typedef _Float16 h4v __attribute__((ext_vector_type(4)));
+constexpr float kLoScale = 2048.0f, kLoUnscale = 1.0f / 2048.0f;
 __device__ __forceinline__ void split4(const float4 x, h4v& hi, h4v& lo) {
   const float v[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     hi[i] = (_Float16)v[i];
-    lo[i] = (_Float16)(v[i] - (float)hi[i]);
+    lo[i] = (_Float16)((v[i] - (float)hi[i]) * kLoScale);
   }
 }
 
@@ -90,10 +96,11 @@ __global__ void __launch_bounds__(kRowThreads) rmsnorm(float* Y, int ldy, const 
 constexpr int BM = 64, BN = 128, BK = 64;
 
 // The product runs on the fp16 matrix cores to fp32 accuracy: each fp32
-// activation a is split into hi = fp16(a) and lo = fp16(a - hi), so that
-// hi + lo = a to about 2^-22 relative, and the weights are fp16 already;
-// hi * W and lo * W accumulate in fp32 (v_mfma_f32_32x32x16_f16, two per
-// k-step of 16, operands read from LDS 16 bytes per lane).  The split happens
+// activation a is split into hi and a scaled lo (split4: a = hi + lo 2^-11
+// to about 2^-22 relative), and the weights are fp16 already; hi * W and
+// lo * W accumulate in two fp32 accumulators (v_mfma_f32_32x32x16_f16, two
+// per k-step of 16, operands read from LDS 16 bytes per lane), added as
+// hi + 2^-11 lo at the end.  The split happens
 // once, when a tile is staged in LDS.  LDS rows hold 72 halves (144 bytes, a
 // multiple of 16 for the 16-byte reads).
 typedef _Float16 h8v __attribute__((ext_vector_type(8)));
@@ -101,7 +108,7 @@ constexpr int HP = BK + 8;
 
 template <bool ADD>
 __global__ void __launch_bounds__(256) gemm16(float* Out, int ldo, const float* A, int lda, const uint16_t* Wm,
-                                              int M, int N, int K) {
+                                              int M, int N, int K, int32_t* state) {
   __shared__ _Float16 Ah[2][BM][HP];
   __shared__ _Float16 Al[2][BM][HP];
   __shared__ uint16_t Bh[2][BN][HP];
@@ -115,6 +122,9 @@ __global__ void __launch_bounds__(256) gemm16(float* Out, int ldo, const float* 
   const int bn = tid >> 1, bk = (tid & 1) * 32;
   float4 ra[4];
   uint4 rb[4];
+  // an activation fp16 cannot carry (|a| > 65504, inf or NaN) is latched as
+  // DEV_RANGE in the status word instead of reaching the KV cache unnoticed
+  bool out_of_range = false;
   auto fetch = [&](int kt) {
     const int k0 = kt * BK;
 #pragma unroll
@@ -148,6 +158,7 @@ __global__ void __launch_bounds__(256) gemm16(float* Out, int ldo, const float* 
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
       h4v hi, lo;
+      out_of_range |= !(fmaxf(fmaxf(fabsf(ra[h].x), fabsf(ra[h].y)), fmaxf(fabsf(ra[h].z), fabsf(ra[h].w))) <= 65504.f);
       split4(ra[h], hi, lo);
       *(h4v*)&Ah[buf][ar + 32 * (h & 1)][ak + 32 * (h >> 1)] = hi;
       *(h4v*)&Al[buf][ar + 32 * (h & 1)][ak + 32 * (h >> 1)] = lo;
@@ -159,11 +170,14 @@ __global__ void __launch_bounds__(256) gemm16(float* Out, int ldo, const float* 
       d[2 * i + 1] = make_uint2(rb[i].z, rb[i].w);
     }
   };
-  f16v acc[2];
+  f16v acc[2], accl[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+    for (int r = 0; r < 16; ++r) {
+      acc[i][r] = 0.f;
+      accl[i][r] = 0.f;
+    }
   fetch(0);
   stash(0);
   __syncthreads();
@@ -181,12 +195,13 @@ __global__ void __launch_bounds__(256) gemm16(float* Out, int ldo, const float* 
         const h8v ah = *(const h8v*)&Ah[buf][32 * i + li][kq];
         const h8v al = *(const h8v*)&Al[buf][32 * i + li][kq];
         acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, b, acc[i], 0, 0, 0);
-        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, b, acc[i], 0, 0, 0);
+        accl[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, b, accl[i], 0, 0, 0);
       }
     }
     if (kt + 1 < nkt) stash(buf ^ 1);
     __syncthreads();
   }
+  if (out_of_range) atomicCAS(state, 0, (int)DEV_RANGE);
   // accumulator layout of a 32x32 tile: lane l, element r holds row
   // 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32
   const int n = n0 + wave * 32 + li;
@@ -198,7 +213,8 @@ __global__ void __launch_bounds__(256) gemm16(float* Out, int ldo, const float* 
       const int m = m0 + 32 * i + 8 * (r >> 2) + 4 * lk + (r & 3);
       if (m < M) {
         float* o = Out + (uint64_t)m * ldo + n;
-        *o = ADD ? *o + acc[i][r] : acc[i][r];
+        const float y = __builtin_fmaf(accl[i][r], kLoUnscale, acc[i][r]);
+        *o = ADD ? *o + y : y;
       }
     }
 }
@@ -376,9 +392,12 @@ __global__ void __launch_bounds__(256) attention_mfma(float* Ao, const float* Qn
     if (t < C) q = *(const float4*)(Qn + (uint64_t)t * qd + (uint64_t)h * HD + 16 * s + 4 * lq);
     split4(q, qh[s], ql[s]);
   }
-  f4v acc[NU];
+  f4v acc[NU], accl[NU];  // P V of the hi and the (scaled) lo parts of P
 #pragma unroll
-  for (int u = 0; u < NU; ++u) acc[u] = f4v{0.f, 0.f, 0.f, 0.f};
+  for (int u = 0; u < NU; ++u) {
+    acc[u] = f4v{0.f, 0.f, 0.f, 0.f};
+    accl[u] = f4v{0.f, 0.f, 0.f, 0.f};
+  }
   float mrow[4], lrow[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
@@ -421,12 +440,15 @@ __global__ void __launch_bounds__(256) attention_mfma(float* Ao, const float* Qn
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
       sc[kt] = f4v{0.f, 0.f, 0.f, 0.f};
+      f4v scl = f4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         const h4v kb = *(const h4v*)(Ks + (kt * 16 + lr) * KS + 16 * s + 4 * lq);
         sc[kt] = __builtin_amdgcn_mfma_f32_16x16x16f16(qh[s], kb, sc[kt], 0, 0, 0);
-        sc[kt] = __builtin_amdgcn_mfma_f32_16x16x16f16(ql[s], kb, sc[kt], 0, 0, 0);
+        scl = __builtin_amdgcn_mfma_f32_16x16x16f16(ql[s], kb, scl, 0, 0, 0);
       }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sc[kt][r] = __builtin_fmaf(scl[r], kLoUnscale, sc[kt][r]);
     }
     // mask (key position > query position, or past the keys) and row maxima
     float bm[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
@@ -463,7 +485,10 @@ __global__ void __launch_bounds__(256) attention_mfma(float* Ao, const float* Qn
 #pragma unroll
     for (int u = 0; u < NU; ++u)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[u][r] *= scale[r];
+      for (int r = 0; r < 4; ++r) {
+        acc[u][r] *= scale[r];
+        accl[u][r] *= scale[r];
+      }
     // the wave's own P tile: its LDS writes must land before its reads
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
     __builtin_amdgcn_wave_barrier();
@@ -477,7 +502,7 @@ __global__ void __launch_bounds__(256) attention_mfma(float* Ao, const float* Qn
       for (int u = 0; u < NU; ++u) {
         const h4v vb = *(const h4v*)(Vt + (16 * u + lr) * VT + 16 * s + 4 * lq);
         acc[u] = __builtin_amdgcn_mfma_f32_16x16x16f16(ph, vb, acc[u], 0, 0, 0);
-        acc[u] = __builtin_amdgcn_mfma_f32_16x16x16f16(pl, vb, acc[u], 0, 0, 0);
+        accl[u] = __builtin_amdgcn_mfma_f32_16x16x16f16(pl, vb, accl[u], 0, 0, 0);
       }
     }
   }
@@ -489,7 +514,7 @@ __global__ void __launch_bounds__(256) attention_mfma(float* Ao, const float* Qn
     float* o = Ao + (uint64_t)t * qd + (uint64_t)h * HD;
     const float inv = 1.0f / lrow[r];
 #pragma unroll
-    for (int u = 0; u < NU; ++u) o[16 * u + lr] = acc[u][r] * inv;
+    for (int u = 0; u < NU; ++u) o[16 * u + lr] = __builtin_fmaf(accl[u][r], kLoUnscale, acc[u][r]) * inv;
   }
 }
 
@@ -515,12 +540,12 @@ __global__ void __launch_bounds__(256) radd(float* R, const float* A, const floa
 using namespace kie;
 
 static hipError_t launch_gemm(bool add, float* Out, int ldo, const float* A, int lda, const uint16_t* Wm, int M, int N,
-                              int K, hipStream_t st) {
+                              int K, int32_t* state, hipStream_t st) {
   const dim3 grid((N + pf::BN - 1) / pf::BN, (M + pf::BM - 1) / pf::BM);
   if (add) {
-    hipLaunchKernelGGL(pf::gemm16<true>, grid, dim3(256), 0, st, Out, ldo, A, lda, Wm, M, N, K);
+    hipLaunchKernelGGL(pf::gemm16<true>, grid, dim3(256), 0, st, Out, ldo, A, lda, Wm, M, N, K, state);
   } else {
-    hipLaunchKernelGGL(pf::gemm16<false>, grid, dim3(256), 0, st, Out, ldo, A, lda, Wm, M, N, K);
+    hipLaunchKernelGGL(pf::gemm16<false>, grid, dim3(256), 0, st, Out, ldo, A, lda, Wm, M, N, K, state);
   }
   return hipGetLastError();
 }
@@ -571,24 +596,24 @@ extern "C" hipError_t kie_internal_prefill_chunk(const PrefillArgs* a, hipStream
     const uint16_t* Wl = a->W + (uint64_t)l * a->pl.layer_stride;
     const float* xin = m.parallel ? Rslot(l - m.delay - 1) : X;
     hipLaunchKernelGGL(pf::rmsnorm, dim3(C), dim3(pf::kRowThreads), 0, st, Y, ly, xin, d, Wl + a->pl.attn_norm, m.eps);
-    if ((e = launch_gemm(false, Gb, lg, Y, ly, Wl + a->pl.wqkv, C, qd + 2 * kvd, d, st)) != hipSuccess) return e;
+    if ((e = launch_gemm(false, Gb, lg, Y, ly, Wl + a->pl.wqkv, C, qd + 2 * kvd, d, a->state, st)) != hipSuccess) return e;
     hipLaunchKernelGGL(pf::rope_kv, dim3(C), dim3(pf::kRowThreads), 0, st, Qn, Gb, lg, a->kv, a->rope, m, l, a->pos0);
     launch_attention(m, l, Ao, Qn, a->kv, a->pos0, C, st);
     if (m.parallel) {
       // P = attn; P += mlp; R_l = R_{l-1} + P
-      if ((e = launch_gemm(false, Pp, d, Ao, qd, Wl + a->pl.wo, C, d, qd, st)) != hipSuccess) return e;
+      if ((e = launch_gemm(false, Pp, d, Ao, qd, Wl + a->pl.wo, C, d, qd, a->state, st)) != hipSuccess) return e;
     } else {
-      if ((e = launch_gemm(true, X, d, Ao, qd, Wl + a->pl.wo, C, d, qd, st)) != hipSuccess) return e;
+      if ((e = launch_gemm(true, X, d, Ao, qd, Wl + a->pl.wo, C, d, qd, a->state, st)) != hipSuccess) return e;
     }
     hipLaunchKernelGGL(pf::rmsnorm, dim3(C), dim3(pf::kRowThreads), 0, st, Y, ly, xin, d, Wl + a->pl.mlp_norm, m.eps);
-    if ((e = launch_gemm(false, Gb, lg, Y, ly, Wl + a->pl.wgu, C, 2 * F, d, st)) != hipSuccess) return e;
+    if ((e = launch_gemm(false, Gb, lg, Y, ly, Wl + a->pl.wgu, C, 2 * F, d, a->state, st)) != hipSuccess) return e;
     hipLaunchKernelGGL(pf::swiglu, dim3(C), dim3(pf::kRowThreads), 0, st, Y, ly, Gb, lg, F);
     if (m.parallel) {
-      if ((e = launch_gemm(true, Pp, d, Y, ly, Wl + a->pl.wd, C, d, F, st)) != hipSuccess) return e;
+      if ((e = launch_gemm(true, Pp, d, Y, ly, Wl + a->pl.wd, C, d, F, a->state, st)) != hipSuccess) return e;
       const int blocks = (int)((Cd + 255) / 256 < 4096 ? (Cd + 255) / 256 : 4096);
       hipLaunchKernelGGL(pf::radd, dim3(blocks), dim3(256), 0, st, Rslot(l), Rslot(l - 1), Pp, Cd);
     } else {
-      if ((e = launch_gemm(true, X, d, Y, ly, Wl + a->pl.wd, C, d, F, st)) != hipSuccess) return e;
+      if ((e = launch_gemm(true, X, d, Y, ly, Wl + a->pl.wd, C, d, F, a->state, st)) != hipSuccess) return e;
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }

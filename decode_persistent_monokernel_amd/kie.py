@@ -17,11 +17,13 @@ from .config import ModelConfig
 from .inputs import LAYER_TENSORS
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libkie.so")
+# KIE_LIBRARY selects another build of the same library (the sanitized
+# host-only build that the CPU tests of the C ABI use)
+LIB_PATH = os.environ.get("KIE_LIBRARY") or os.path.join(_PKG, "libkie.so")
 
 KIE_OK = 0
 STATUS = {0: "ok", -1: "invalid argument", -2: "HIP error", -3: "capacity", -4: "state",
-          -5: "timeout", -6: "unsupported", -7: "bad token"}
+          -5: "timeout", -6: "unsupported", -7: "bad token", -8: "fp16 range"}
 
 
 class KieError(RuntimeError):
@@ -93,6 +95,20 @@ def lib() -> C.CDLL:
             getattr(L, name).restype = C.c_int
         _lib = L
     return _lib
+
+
+def unload() -> None:
+    """Unload the library (its kernels' code objects are unregistered from
+    the HIP runtime now, while the runtime is fully up, rather than by exit
+    handlers at interpreter teardown).  Every context must be destroyed
+    first; lib() loads it again."""
+    global _lib
+    if _lib is None:
+        return
+    import _ctypes
+    h = _lib._handle
+    _lib = None
+    _ctypes.dlclose(h)
 
 
 def config_c(cfg: ModelConfig, max_ctx: Optional[int] = None) -> ModelConfigC:

@@ -57,7 +57,8 @@ typedef enum kie_status {
   KIE_ERR_STATE = -4,       /* memory not bound / weights not loaded / no device */
   KIE_ERR_TIMEOUT = -5,     /* a wait inside the kernel exceeded the timeout */
   KIE_ERR_UNSUPPORTED = -6, /* valid model that this kernel build cannot run */
-  KIE_ERR_BAD_TOKEN = -7    /* a token id outside [0, vocab) reached the kernel */
+  KIE_ERR_BAD_TOKEN = -7,   /* a token id outside [0, vocab) reached the kernel */
+  KIE_ERR_RANGE = -8        /* kie_prefill_batched met an activation outside the fp16 range */
 } kie_status;
 
 /* Model shape.  Rules (KIE_ERR_INVALID_ARG otherwise): all sizes > 0;
@@ -120,15 +121,31 @@ kie_status kie_query_sizes(const kie_ctx* ctx, size_t* packed_weight_bytes, size
 kie_status kie_bind_memory(kie_ctx* ctx, void* d_packed, void* d_kv, void* d_workspace);
 
 /* Pack the host weights into the kernel layout and upload them (blocking
- * with respect to the host: the host arrays may be freed on return). */
+ * with respect to the host: the host arrays may be freed on return).  The
+ * weights stay fp16 exactly as given: the pages' results are for FP16
+ * decoding with no quantization or pruning (Malay and Vietnamese explainers,
+ * results table "Laneformer 2B"), and decoding at batch 1 is bound by reading
+ * every weight from memory once per token (Chinese feature, on decode being
+ * memory-bandwidth bound), so the layout only reorders them for 16-byte
+ * coalesced loads (row pairs in 1-KB chunks; RoPE partners and gate/up rows
+ * paired) and adds nothing.  src must hold every pointer of kie_weights
+ * (KIE_ERR_INVALID_ARG otherwise); KIE_ERR_STATE before kie_bind_memory;
+ * KIE_ERR_HIP if an upload fails. */
 kie_status kie_load_weights(kie_ctx* ctx, const kie_weights* host_src, void* stream);
 
 /* Run the prompt d_prompt[0..n_prompt) (device int32 ids) at positions
  * pos..pos+n_prompt-1 (pos is 0 after binding), fill the KV cache and write
  * the greedy next token t1 to *d_next_token (device, may be NULL) and the
  * last position's logits [vocab] to d_logits (device fp32, may be NULL).
- * Afterwards position += n_prompt and t1 is the pending input token.
- * Long prompts are split into several launches internally. */
+ * Afterwards position += n_prompt and t1 is the pending input token.  The
+ * prompt runs through the same persistent decode kernel, one position per
+ * step, with the LM head only at the last position: the pages' monokernel
+ * covers prefill as well as decode and LM-head sampling in one persistent
+ * program (Czech explainer, "Software versus silicon" section).  Long
+ * prompts are split into several launches (kie_set_launch_steps).
+ * KIE_ERR_INVALID_ARG for an empty prompt, KIE_ERR_CAPACITY if
+ * pos + n_prompt > max_ctx, KIE_ERR_STATE if memory or weights are missing;
+ * an id outside [0, vocab) latches KIE_ERR_BAD_TOKEN (kie_sync_status). */
 kie_status kie_prefill(kie_ctx* ctx, const int32_t* d_prompt, int32_t n_prompt, int32_t* d_next_token,
                        float* d_logits, void* stream);
 
@@ -139,15 +156,18 @@ kie_status kie_prefill_scratch_bytes(const kie_ctx* ctx, int32_t chunk_tokens, s
 /* kie_prefill with the prompt batched: the same result (KV cache rows for
  * positions pos..pos+n_prompt-1, t1, the last position's logits, position
  * += n_prompt), computed as dense products on the matrix cores.  The pages'
- * monokernel runs prefill on the GPU (Kog explainer, "Monokernel" section);
- * batching the prompt reads every weight once per chunk of tokens instead
- * of once per token.  All prompt tokens but the last go through batched
- * GEMMs (fp32 activations, fp16 weights, fp32 accumulation; on the fp16
- * matrix cores, each activation entering as an fp16 hi + lo pair, so the
- * products keep fp32 accuracy to ~2^-22), RoPE, fp16 KV append and causal
- * attention (likewise), chunk by chunk; the last one runs through
+ * monokernel runs prefill on the GPU (Czech explainer, "Software versus
+ * silicon" section); batching the prompt reads every weight once per chunk
+ * of tokens instead of once per token.  All prompt tokens but the last go
+ * through batched GEMMs (fp32 activations, fp16 weights, fp32 accumulation;
+ * on the fp16 matrix cores, each activation a entering as hi = fp16(a) and
+ * lo = fp16((a - hi) * 2^11), the two products accumulated apart and added
+ * as hi + 2^-11 lo, so they keep fp32 accuracy to ~2^-22 relative for
+ * 2^-14 <= |a| <= 65504 and to ~2^-25 absolute below), RoPE, fp16 KV append
+ * and causal attention (likewise), chunk by chunk; the last one runs through
  * the decode kernel, which yields t1 (greedy or sampled, see
- * kie_set_sampling).  d_scratch is caller-owned device memory (16-byte
+ * kie_set_sampling).  An activation above 65504 in magnitude (or not
+ * finite) cannot be split: it latches KIE_ERR_RANGE (kie_sync_status).  d_scratch is caller-owned device memory (16-byte
  * aligned) of scratch_bytes; the chunk is the largest that fits, at most
  * 2048 tokens (kie_prefill_scratch_bytes gives the size for a chunk).  The
  * lane-structured block keeps its delayed residual (layer l reads
@@ -158,7 +178,13 @@ kie_status kie_prefill_scratch_bytes(const kie_ctx* ctx, int32_t chunk_tokens, s
 kie_status kie_prefill_batched(kie_ctx* ctx, const int32_t* d_prompt, int32_t n_prompt, int32_t* d_next_token,
                                float* d_logits, void* d_scratch, size_t scratch_bytes, void* stream);
 
-/* Run n_tokens decode steps.  Step k consumes d_forced_in[k] when that
+/* Run n_tokens decode steps inside one persistent kernel launch per
+ * kie_set_launch_steps steps: the pages' monokernel, one program for the
+ * whole decode loop with no kernel launches between layers or tokens and no
+ * grid synchronisations (Malay and Vietnamese explainers, "Monokernel"
+ * bullet; Czech explainer, "Software versus silicon" section), emitting
+ * tokens of a single request at batch 1 (results table "Laneformer 2B").
+ * Step k consumes d_forced_in[k] when that
  * pointer is not NULL (teacher forcing), else the previous step's argmax (the
  * pending token for k = 0); it runs at position pos + k, writes its greedy
  * (or sampled, see kie_set_sampling) token to d_tokens_out[k] (device, may be NULL) and, when d_logits_out is not
@@ -199,8 +225,12 @@ kie_status kie_set_timeout_us(kie_ctx* ctx, uint64_t microseconds);
  * or non-finite temperature (the setting is then left unchanged). */
 kie_status kie_set_sampling(kie_ctx* ctx, float temperature, uint64_t seed);
 
-/* Debug flags (bit 0: one workgroup waits on a word nobody writes, which
- * must end in KIE_ERR_TIMEOUT, not a hang).  0 = normal operation. */
+/* Debug flags.  Bit 0: one workgroup waits on a word nobody writes, which
+ * must end in KIE_ERR_TIMEOUT, not a hang.  Bit 1: race-detection jitter,
+ * every wave sleeps a pseudo-random 0..6 us at the start of every phase
+ * (hashed from workgroup, wave, step and phase), which reorders the
+ * workgroups' arrivals at every exchange; the results must stay bitwise
+ * identical.  0 = normal operation. */
 kie_status kie_set_debug_flags(kie_ctx* ctx, uint32_t flags);
 
 /* Phase trace for performance analysis.  When d_trace is not NULL, the

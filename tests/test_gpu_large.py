@@ -131,15 +131,20 @@ def fp16_ulp(a):
     return 2.0 ** (e - 10)
 
 
-def assert_kv_close(gpu, ref, name):
+def assert_kv_close(gpu, ref, name, pre_round=None):
     """the GPU's fp16 rows against the exact (fp64) values: one rounding to
     binary16 of a value computed in fp32.  Allowed: one fp16 ulp, or 5e-5
     absolute for small values, where the fp32 dot product over d terms of
-    size ~0.02 (error ~1e-5) is coarser than the fp16 spacing."""
+    size ~0.02 (error ~1e-5) is coarser than the fp16 spacing.  pre_round,
+    for rows of a later layer, is the fp32 error of the value before its
+    rounding relative to the rows' RMS: one ulp plus that much is allowed."""
     g = gpu.astype(np.float64)
     r = np.asarray(ref, dtype=np.float64)
     err = np.abs(g - r)
-    tol = np.maximum(fp16_ulp(r), 5e-5)
+    if pre_round is None:
+        tol = np.maximum(fp16_ulp(r), 5e-5)
+    else:
+        tol = fp16_ulp(r) + pre_round * float(np.sqrt(np.mean(r * r)))
     bad = err > tol
     worst = np.argsort((err / tol).ravel())[-3:]
     say(f"[{name}] max |gpu - oracle| {err.max():.3e}; worst err/tol {np.round((err / tol).ravel()[worst], 3)} "
@@ -178,23 +183,4 @@ def test_bench_configuration():
     c_tok, c_lg = eng.decode(N, want_logits=True)
     assert np.array_equal(a_tok, c_tok)
     assert np.array_equal(a_lg.view(np.uint32), c_lg.view(np.uint32))
-    eng.close()
-
-
-def test_cfg4_rope_over_32k_prompt():
-    """cfg4's RoPE base (5e5) and width over its whole 32768-token prompt,
-    with two layers: layer-0 keys and values at sampled positions"""
-    cfg = CFG4.with_(name="cfg4-2L", n_layers=2)
-    P = cfg.prompt_len
-    say(f"case cfg4 layer-0 KV over a {P}-token prompt (2 layers)")
-    w = gen_weights(cfg)
-    prompt = gen_prompt(cfg, n=P)
-    eng = make_engine(cfg, P + 1)
-    eng.set_launch_steps(4096)
-    eng.load_weights(w)
-    eng.prefill(prompt)
-    pos = np.unique(np.concatenate([np.arange(0, 4), np.arange(4, P, 1021), [P - 1]]))
-    kref, vref = layer0_kv_reference(cfg, w, prompt, pos)
-    assert_kv_close(gpu_kv_rows(eng, cfg, 0, 0, pos), kref, "cfg4 layer-0 K")
-    assert_kv_close(gpu_kv_rows(eng, cfg, 0, 1, pos), vref, "cfg4 layer-0 V")
     eng.close()

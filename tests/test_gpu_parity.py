@@ -163,6 +163,36 @@ def test_deterministic_and_resumable():
     eng.close()
 
 
+@pytest.mark.parametrize("shape", [
+    dict(name="mha", seed_index=17),
+    dict(name="gqa4", n_heads=8, n_kv_heads=2, head_dim=32, seed_index=18),
+    dict(name="lanes", n_layers=5, n_lanes=2, lane_delay=2, sequential=False, seed_index=19),
+], ids=lambda s: s["name"])
+def test_jitter_keeps_results_bitwise(shape):
+    """race detection: with every wave sleeping a pseudo-random time at every
+    phase start (a different pattern in every launch), the logits of a
+    teacher-forced decode stay bitwise identical to an undisturbed run; the
+    first differing repeat fails"""
+    cfg = CFG0.with_(prompt_len=9, decode_steps=12, **shape)
+    say(f"case jitter bitwise repeat ({shape['name']})")
+    w = gen_weights(cfg, overrides={"wq": 0.1, "wk": 0.1})
+    prompt = gen_prompt(cfg)
+    eng = make_engine(cfg, cfg.max_ctx)
+    eng.load_weights(w)
+    t1 = eng.prefill(prompt)
+    forced = list(np.random.default_rng(3).integers(0, cfg.vocab, cfg.decode_steps))
+    a_tok, a_lg = eng.decode(cfg.decode_steps, forced=forced, want_logits=True)
+    eng.set_debug_flags(2)
+    for rep in range(4):
+        eng.set_position(len(prompt), t1)
+        eng.set_launch_steps(cfg.decode_steps if rep % 2 == 0 else 5)
+        b_tok, b_lg = eng.decode(cfg.decode_steps, forced=forced, want_logits=True)
+        assert np.array_equal(a_lg.view(np.uint32), b_lg.view(np.uint32)), f"repeat {rep} differs"
+        assert np.array_equal(a_tok, b_tok)
+    eng.set_debug_flags(0)
+    eng.close()
+
+
 def test_bounded_wait_reports_timeout():
     """a workgroup waits on a word nobody writes: the launch must end with
     KIE_ERR_TIMEOUT, not hang, and the context must work again afterwards"""

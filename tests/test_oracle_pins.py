@@ -486,3 +486,46 @@ def test_planted_gumbel_sign_mistake_is_caught(monkeypatch):
     monkeypatch.setattr(O, "gumbel_noise", wrong)
     with pytest.raises(AssertionError):
         test_gumbel_max_matches_softmax_chi_square()
+
+
+def test_sampling_scores_argmax_is_the_sample():
+    # the scores the GPU path maximises (logits / T plus the noise) pick the
+    # same token as the sampler, over many seeds, positions and temperatures
+    rng = np.random.default_rng(11)
+    for k in range(300):
+        l = rng.normal(size=97) * rng.uniform(0.1, 3.0)
+        T = float(rng.choice([0.0, 0.3, 0.8, 2.5]))
+        seed = int(rng.integers(0, 2 ** 63))
+        pos = int(rng.integers(0, 40000))
+        sc = O.sampling_scores(l, T, seed, pos)
+        assert int(np.argmax(sc)) == O.sample(l, T, seed, pos)
+        if T == 0:
+            assert np.array_equal(sc, l)
+
+
+def test_gumbel_noise_moments():
+    # standard Gumbel: mean = Euler-Mascheroni constant, variance = pi^2 / 6
+    # (200,000 rows of one position; 5 standard errors of slack)
+    g = O.gumbel_noise(0xfeed, 123, 200_000)
+    assert abs(g.mean() - 0.5772156649) < 0.015, g.mean()
+    assert abs(g.var() - math.pi ** 2 / 6) < 0.04, g.var()
+    # its distribution function exp(-exp(-x)) at a few points
+    for x in (-1.0, 0.0, 1.0, 3.0):
+        assert abs(np.mean(g <= x) - math.exp(-math.exp(-x))) < 0.005
+
+
+def test_layer1_kv_helper_matches_the_prefill_cache():
+    # the GPU tests' cheap layer-1 K/V reference (attention at sampled rows
+    # only) equals the cache the oracle's full prefill writes
+    from paritylib import layer1_kv_reference
+    cfg = CFG0.with_(n_heads=4, n_kv_heads=2, seed_index=77)
+    w = gen_weights(cfg, std=0.1)
+    prompt = gen_prompt(cfg, n=40)
+    for kv16 in (False, True):
+        orc = O.Oracle(cfg, w, kv_fp16=kv16)
+        cache = orc.new_cache(40)
+        orc.prefill(cache, prompt)
+        pos = np.array([0, 1, 17, 39])
+        k1, v1 = (orc.cache_round(a) for a in layer1_kv_reference(orc, prompt, pos))
+        assert rel(k1, cache.K[1][:, pos, :].transpose(1, 0, 2)) < 1e-12
+        assert rel(v1, cache.V[1][:, pos, :].transpose(1, 0, 2)) < 1e-12
