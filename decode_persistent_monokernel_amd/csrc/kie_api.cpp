@@ -17,6 +17,7 @@ extern "C" hipError_t kie_internal_launch(const kie::KParams* kp, int nwg, size_
 extern "C" hipError_t kie_internal_zero(void* p, size_t bytes, hipStream_t stream);
 extern "C" hipError_t kie_internal_occupancy(int G, int parallel, size_t lds_bytes, int* blocks_per_cu);
 extern "C" hipError_t kie_internal_prefill_chunk(const kie::PrefillArgs* a, hipStream_t stream);
+extern "C" hipError_t kie_internal_noalloc_scratch(int device, void** ptr);
 
 struct kie_ctx {
   kie_model_config cfg;
@@ -39,6 +40,7 @@ struct kie_ctx {
   uint64_t seed = 0;
   int32_t launch_steps = 512;
   uint64_t* trace = nullptr;
+  void* noalloc_scratch = nullptr;  // this device's kie_prefill_batched_noalloc scratch
   int32_t trace_steps = 0;
   double clock_khz = 100000.0;
   std::string err;
@@ -268,6 +270,16 @@ kie_status kie_create(const kie_model_config* cfg, int device, kie_ctx** out) {
       return KIE_ERR_UNSUPPORTED;
     }
   }
+  if (device >= 0) {
+    // the device address of this GPU's no-allocation scratch (the device is
+    // current: hipSetDevice above)
+    const hipError_t e = kie_internal_noalloc_scratch(device, &c->noalloc_scratch);
+    if (e != hipSuccess) {
+      std::fprintf(stderr, "kie_create: no-allocation scratch: %s\n", hipGetErrorString(e));
+      delete c;
+      return KIE_ERR_HIP;
+    }
+  }
   c->pl = kie::pack_layout(c->m);
   c->wl = kie::ws_layout(c->m, c->nwg);
   c->lp = kie::lds_plan(c->m, c->nwg);
@@ -367,8 +379,9 @@ kie_status kie_prefill_scratch_bytes(const kie_ctx* c, int32_t chunk_tokens, siz
   return KIE_OK;
 }
 
-kie_status kie_prefill_batched(kie_ctx* c, const int32_t* d_prompt, int32_t n, int32_t* d_next, float* d_logits,
-                               void* d_scratch, size_t scratch_bytes, void* stream) {
+namespace {
+kie_status prefill_batched(kie_ctx* c, const int32_t* d_prompt, int32_t n, int32_t* d_next, float* d_logits,
+                           void* d_scratch, size_t scratch_bytes, void* stream) {
   kie_status s = ready(c);
   if (s != KIE_OK) return s;
   if (!d_prompt || n <= 0) return fail(c, KIE_ERR_INVALID_ARG, "empty prompt");
@@ -405,6 +418,25 @@ kie_status kie_prefill_batched(kie_ctx* c, const int32_t* d_prompt, int32_t n, i
   // the last prompt token goes through the decode kernel: LM head, the
   // greedy or sampled t1, its logits, and the pending-token state
   return kie_prefill(c, d_prompt + n - 1, 1, d_next, d_logits, stream);
+}
+}  // namespace
+
+kie_status kie_prefill_batched(kie_ctx* c, const int32_t* d_prompt, int32_t n, int32_t* d_next, float* d_logits,
+                               void* d_scratch, size_t scratch_bytes, void* stream) {
+  return prefill_batched(c, d_prompt, n, d_next, d_logits, d_scratch, scratch_bytes, stream);
+}
+
+kie_status kie_prefill_batched_noalloc(kie_ctx* c, const int32_t* d_prompt, int32_t n, int32_t* d_next,
+                                       float* d_logits, void* stream) {
+  kie_status s = ready(c);
+  if (s != KIE_OK) return s;
+  if (!c->noalloc_scratch) return fail(c, KIE_ERR_STATE, "no-allocation scratch not available on this device");
+  const uint64_t per_token = kie::pf_floats_per_token(c->m) * sizeof(float);
+  if (per_token > kie::kNoAllocScratchBytes)
+    return fail(c, KIE_ERR_UNSUPPORTED,
+                "one prompt token needs " + std::to_string(per_token) + " bytes of prefill scratch, more than the " +
+                    std::to_string(kie::kNoAllocScratchBytes) + " bytes of the no-allocation scratch");
+  return prefill_batched(c, d_prompt, n, d_next, d_logits, c->noalloc_scratch, kie::kNoAllocScratchBytes, stream);
 }
 
 kie_status kie_decode(kie_ctx* c, int32_t n, int32_t* d_out, const int32_t* d_forced, float* d_logits,

@@ -1,4 +1,4 @@
-// Host-only stand-ins for the four launch helpers that the HIP sources
+// Host-only stand-ins for the five device-side helpers that the HIP sources
 // define, for the sanitizer build of the host library (kie_api.cpp compiled
 // with the host compiler under AddressSanitizer and UndefinedBehaviorSanitizer).
 // That build runs the CPU tests of the C ABI: argument checks, sizes, the
@@ -16,3 +16,4 @@ extern "C" hipError_t kie_internal_occupancy(int, int, size_t, int*) { return hi
 extern "C" hipError_t kie_internal_prefill_chunk(const kie::PrefillArgs*, hipStream_t) {
   return hipErrorNoBinaryForGpu;
 }
+extern "C" hipError_t kie_internal_noalloc_scratch(int, void**) { return hipErrorNoBinaryForGpu; }

@@ -446,6 +446,11 @@ KIE_HD uint64_t pf_floats_per_token(const Dims& m) {
          (m.parallel ? (uint64_t)(m.delay + 3) * m.d : 0ull);
 }
 
+// the no-allocation batched prefill's scratch: one array of this many bytes
+// per GPU, held until the process ends; devices numbered below kMaxDevices
+constexpr uint64_t kNoAllocScratchBytes = 64ull << 20;
+constexpr int kMaxDevices = 64;
+
 enum DebugFlags : uint32_t {
   DBG_WAIT_NEVER = 1u,  // workgroup 0 waits on a word no one writes (timeout test)
   DBG_JITTER = 2u,      // every wave sleeps a pseudo-random time at every phase start

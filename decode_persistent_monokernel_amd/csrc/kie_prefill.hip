@@ -18,6 +18,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "kie_layout.h"
 
 namespace kie {
@@ -538,6 +540,30 @@ __global__ void __launch_bounds__(256) radd(float* R, const float* A, const floa
 }  // namespace kie
 
 using namespace kie;
+
+// Scratch of kie_prefill_batched_noalloc: one array per GPU, part of the
+// library's code object, so that callers that cannot allocate device memory
+// (HIP graph capture, tight serving loops) can still run the batched
+// prefill.  Its host-side name is not a device address: host code uses the
+// pointer kie_internal_noalloc_scratch() obtains for the current device.
+static __device__ __align__(256) float scratch[kNoAllocScratchBytes / sizeof(float)];
+
+// The device address of `scratch` on `device` (which must be the current
+// device), looked up once per device and kept.  Thread-safe.
+extern "C" hipError_t kie_internal_noalloc_scratch(int device, void** ptr) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  if (device < 0 || device >= kMaxDevices || !ptr) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[device]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[device] = p;
+  }
+  *ptr = addr[device];
+  return hipSuccess;
+}
 
 static hipError_t launch_gemm(bool add, float* Out, int ldo, const float* A, int lda, const uint16_t* Wm, int M, int N,
                               int K, int32_t* state, hipStream_t st) {

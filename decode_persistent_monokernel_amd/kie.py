@@ -67,6 +67,7 @@ def lib() -> C.CDLL:
         L.kie_prefill.argtypes = [vp, vp, i32, vp, vp, vp]
         L.kie_prefill_scratch_bytes.argtypes = [vp, i32, C.POINTER(sz)]
         L.kie_prefill_batched.argtypes = [vp, vp, i32, vp, vp, vp, sz, vp]
+        L.kie_prefill_batched_noalloc.argtypes = [vp, vp, i32, vp, vp, vp]
         L.kie_decode.argtypes = [vp, i32, vp, vp, vp, vp]
         L.kie_set_position.argtypes = [vp, i32, i32, vp]
         L.kie_sync_status.argtypes = [vp, vp]
@@ -88,7 +89,8 @@ def lib() -> C.CDLL:
         L.kie_destroy.argtypes = [vp]
         L.kie_destroy.restype = None
         for name in ("kie_create", "kie_query_sizes", "kie_bind_memory", "kie_load_weights",
-                     "kie_prefill", "kie_prefill_scratch_bytes", "kie_prefill_batched", "kie_decode", "kie_set_position", "kie_sync_status",
+                     "kie_prefill", "kie_prefill_scratch_bytes", "kie_prefill_batched", "kie_prefill_batched_noalloc",
+                     "kie_decode", "kie_set_position", "kie_sync_status",
                      "kie_set_timeout_us", "kie_set_debug_flags", "kie_set_sampling", "kie_set_launch_steps",
                      "kie_set_trace",
                      "kie_pack_weights_host", "kie_launch_info", "kie_validate_schedule"):
@@ -329,6 +331,22 @@ class Engine:
         _check(self.L.kie_prefill_batched(self.ctx, d_prompt.data_ptr(), len(prompt), d_next.data_ptr(),
                                           d_logits.data_ptr() if d_logits is not None else None,
                                           scratch.data_ptr(), int(nbytes.value), self.stream()), self.ctx)
+        self.sync()
+        tok = int(d_next.cpu()[0])
+        if want_logits:
+            return tok, d_logits.cpu().numpy()
+        return tok
+
+    def prefill_batched_noalloc(self, prompt: Sequence[int], want_logits: bool = False):
+        """kie_prefill_batched_noalloc: the batched prefill on the library's
+        own fixed scratch (no device allocation inside the call)"""
+        t = self.torch
+        d_prompt = self._ids(prompt)
+        d_next = t.empty(1, dtype=t.int32, device=self.dev)
+        d_logits = t.empty(self.cfg.vocab, dtype=t.float32, device=self.dev) if want_logits else None
+        _check(self.L.kie_prefill_batched_noalloc(self.ctx, d_prompt.data_ptr(), len(prompt), d_next.data_ptr(),
+                                                  d_logits.data_ptr() if d_logits is not None else None,
+                                                  self.stream()), self.ctx)
         self.sync()
         tok = int(d_next.cpu()[0])
         if want_logits:

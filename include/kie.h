@@ -178,6 +178,22 @@ kie_status kie_prefill_scratch_bytes(const kie_ctx* ctx, int32_t chunk_tokens, s
 kie_status kie_prefill_batched(kie_ctx* ctx, const int32_t* d_prompt, int32_t n_prompt, int32_t* d_next_token,
                                float* d_logits, void* d_scratch, size_t scratch_bytes, void* stream);
 
+/* kie_prefill_batched without a caller scratch buffer, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  The chunk activations live in a
+ * fixed array of 64 MiB per GPU inside the library (held until the process
+ * ends; its device address is looked up once per device by kie_create), so
+ * the chunk is the largest that fits it, at most 2048 tokens.  This call
+ * allocates nothing and frees nothing.  Every call on one GPU shares that
+ * GPU's array and leaves its contents behind (every value is written before
+ * it is read, so nothing needs clearing): calls that overlap in time on one
+ * GPU, from two streams or two contexts, race and must be serialised by the
+ * caller.  Result, status and errors as kie_prefill_batched;
+ * KIE_ERR_UNSUPPORTED if one prompt token needs more scratch than the array
+ * holds. */
+kie_status kie_prefill_batched_noalloc(kie_ctx* ctx, const int32_t* d_prompt, int32_t n_prompt,
+                                       int32_t* d_next_token, float* d_logits, void* stream);
+
 /* Run n_tokens decode steps inside one persistent kernel launch per
  * kie_set_launch_steps steps: the pages' monokernel, one program for the
  * whole decode loop with no kernel launches between layers or tokens and no
