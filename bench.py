@@ -171,8 +171,6 @@ def summarize_traffic(fetch_dir: str, write_dir: str, copy_bytes: int, cfg_name:
 # ---------------------------------------------------------------------------
 # per-phase critical path from the kernel's own wall-clock stamps
 # ---------------------------------------------------------------------------
-PHASE_NAMES_SEQ = ("QKV", "attention", "O", "gate/up", "down")
-PHASE_NAMES_PAR = ("QKV", "gate/up", "attention", "O", "down")
 END_PHASE = 5 * 64 + 1
 
 
@@ -189,9 +187,13 @@ def phase_trace_summary(tr: np.ndarray, cfg, untraced_ms_per_token: float, comma
     token gather, acquire) follows the LM head.  Per workgroup: the share of
     its time spent between a phase's start and its input being ready (waiting
     on other workgroups), the analogue of a grid-synchronisation share."""
+    from decode_persistent_monokernel_amd import kie
     tick_us = 0.01
     L = cfg.n_layers
-    names = PHASE_NAMES_SEQ if cfg.sequential else PHASE_NAMES_PAR
+    # phase index -> kind name, in the kernel's order (pipelined for the
+    # lane block with a delayed residual)
+    order = [kie.PHASE_KIND_NAMES[k] for k, _ in kie.phase_order(cfg, tr.shape[2])]
+    names = tuple(dict.fromkeys(order[:5 * L]))
     steps = list(range(1, tr.shape[0]))  # the launch's first step also fills the ring: left out
     phases = list(range(5 * L)) + [5 * L]
     hop = {n: [] for n in names + ("LM head",)}
@@ -204,7 +206,7 @@ def phase_trace_summary(tr: np.ndarray, cfg, untraced_ms_per_token: float, comma
         prev_end = start
         waited = np.zeros(tr.shape[2])
         for ph in phases:
-            nm = "LM head" if ph == 5 * L else names[ph % 5]
+            nm = order[ph]
             st = t[ph]
             r_max, e_max = st[:, 1].max(), st[:, 3].max()
             hop[nm].append((r_max - prev_end) * tick_us)
@@ -221,9 +223,11 @@ def phase_trace_summary(tr: np.ndarray, cfg, untraced_ms_per_token: float, comma
         tok_us.append(total)
         wait_share.append(float(np.mean(waited * tick_us / total)))
     T = float(np.mean(tok_us))
+    seq = " ".join(f"{n}_{l}" for n, l in zip(order[:12], [l for _, l in kie.phase_order(cfg, tr.shape[2])][:12]))
     out = [f"# Per-phase critical path of one decode token ({cfg.name}, {cfg.n_layers} layers)", "",
            "From the kernel's own phase stamps (`kie_set_trace`, wall clock at 100 MHz) over "
            f"{len(steps)} decode steps; the stamps are kept in LDS and written out at the end of each step.", "",
+           f"Phase order of a step (`kie_phase_order`): {seq} ...", "",
            "Command (from the repository root, on an MI355X):", "", "```", command, "```", "",
            f"- traced token time: {T:.1f} us (untraced, same run: {untraced_ms_per_token * 1e3:.1f} us)",
            f"- per layer: {T / L:.2f} us",

@@ -94,6 +94,49 @@ kie::Dims make_dims(const kie_model_config& c) {
   return m;
 }
 
+// The phase order of a step (phase_at) against what each phase reads:
+// every (kind, layer) once; QKV after the down projection that published its
+// x; attention after its QKV; O after its attention; gate/up (sequential
+// block) after O; down after its gate/up and its O.  Where the parallel block
+// stages inputs in LDS (LdsPlan::hb) also: gate/up right after its QKV (the
+// QKV prologue writes gate/up's input), O and down of a layer adjacent (the
+// O prologue writes down's input, the O epilogue the rows down adds), and the
+// QKV that an O prologue stages for after that O, with no other O between.
+std::string check_phase_order(const kie::Dims& m, const kie::LdsPlan& lp) {
+  const int L = m.L;
+  std::vector<int> at(5 * (size_t)L, -1);  // (kind, layer) -> phase
+  for (int ph = 0; ph < 5 * L; ++ph) {
+    int k, l;
+    kie::phase_at(lp.pipe, m.parallel, L, ph, &k, &l);
+    if (k < 0 || k >= 5 || l < 0 || l >= L || at[5 * (size_t)l + k] >= 0) return "phase order repeats a phase";
+    at[5 * (size_t)l + k] = ph;
+  }
+  auto P = [&](int k, int l) { return at[5 * (size_t)l + k]; };
+  const bool staged = m.parallel && lp.hb >= 0 && m.G <= 2;
+  for (int l = 0; l < L; ++l) {
+    // the down projection that publishes the QKV input of layer l
+    const int src = m.parallel ? (l > m.delay ? l - m.delay - 1 : -1) : l - 1;
+    if (src >= 0 && P(kie::PH_DOWN, src) > P(kie::PH_QKV, l)) return "QKV before its input";
+    if (P(kie::PH_ATTN, l) < P(kie::PH_QKV, l)) return "attention before its QKV";
+    if (P(kie::PH_O, l) < P(kie::PH_ATTN, l)) return "O before its attention";
+    if (!m.parallel && P(kie::PH_GU, l) < P(kie::PH_O, l)) return "gate/up before O";
+    if (m.parallel && src >= 0 && P(kie::PH_DOWN, src) > P(kie::PH_GU, l)) return "gate/up before its input";
+    if (P(kie::PH_DOWN, l) < P(kie::PH_GU, l) || P(kie::PH_DOWN, l) < P(kie::PH_O, l)) return "down before its inputs";
+    if (!staged) continue;
+    if (P(kie::PH_GU, l) != P(kie::PH_QKV, l) + 1) return "gate/up not right after its QKV";
+    if (P(kie::PH_DOWN, l) != P(kie::PH_O, l) + 1) return "down not right after its O";
+    const int ln = l + 1 + lp.pipe;  // the layer whose input the O prologue of layer l stages
+    if (ln < L) {
+      if (P(kie::PH_QKV, ln) < P(kie::PH_O, l)) return "staged QKV before the O that stages it";
+      if (l + 1 < L && P(kie::PH_O, l + 1) < P(kie::PH_QKV, ln)) return "staged input overwritten before its QKV";
+      const bool stage_x = m.delay > lp.pipe;  // as in the kernel: else the QKV polls x itself
+      if (stage_x && ln > m.delay && P(kie::PH_DOWN, ln - m.delay - 1) > P(kie::PH_O, l))
+        return "input staged before it is published";
+    }
+  }
+  return "";
+}
+
 std::string check_supported(const kie::Dims& m, int nwg) {
   if (m.G != 1 && m.G != 2 && m.G != 4) return "query heads per KV head must be 1, 2 or 4";
   if (m.hd / 8 > 64) return "head_dim above 512 is not supported";
@@ -101,6 +144,8 @@ std::string check_supported(const kie::Dims& m, int nwg) {
   if (m.Hkv > nwg) return "more KV heads than workgroups";
   const kie::LdsPlan lp = kie::lds_plan(m, nwg);
   if (lp.total_floats > kie::kMainFloats) return "model needs more LDS than the kernel reserves";
+  const std::string po = check_phase_order(m, lp);
+  if (!po.empty()) return po;
   const uint64_t lim = 0x7FFFFFFFull;
   if ((uint64_t)m.Hkv * (uint64_t)(m.max_ctx + 1) * (uint64_t)nwg > lim) return "KV heads x context too large";
   if ((uint64_t)m.V * (uint64_t)nwg > lim || (uint64_t)2 * m.F * (uint64_t)nwg > lim)
@@ -527,6 +572,23 @@ kie_status kie_set_trace(kie_ctx* c, void* d_trace, int32_t steps) {
   if (!c || steps < 0 || (steps > 0 && !d_trace)) return KIE_ERR_INVALID_ARG;
   c->trace = (uint64_t*)d_trace;
   c->trace_steps = d_trace ? steps : 0;
+  return KIE_OK;
+}
+
+kie_status kie_phase_order(const kie_model_config* cfg, int32_t nwg, int32_t* kind, int32_t* layer, int32_t n) {
+  if (!cfg || nwg <= 0 || !kind || !layer || !check_config(*cfg).empty()) return KIE_ERR_INVALID_ARG;
+  const kie::Dims m = make_dims(*cfg);
+  if (n < 5 * m.L + 1) return KIE_ERR_INVALID_ARG;
+  if (!check_supported(m, nwg).empty()) return KIE_ERR_UNSUPPORTED;
+  const kie::LdsPlan lp = kie::lds_plan(m, nwg);
+  for (int ph = 0; ph < 5 * m.L; ++ph) {
+    int k, l;
+    kie::phase_at(lp.pipe, m.parallel, m.L, ph, &k, &l);
+    kind[ph] = k;
+    layer[ph] = l;
+  }
+  kind[5 * m.L] = kie::PH_LM;
+  layer[5 * m.L] = m.L;
   return KIE_OK;
 }
 

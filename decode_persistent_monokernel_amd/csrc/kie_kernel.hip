@@ -563,6 +563,7 @@ struct Cursor {
   uint32_t stride;  // bytes from one chunk (attention: key step) to the next
   int rem;          // chunks left in this stretch (attention: 2 per key step)
   int attn, kvh, seg, ph, nph, done;
+  int layer;        // layer of the phase ph
 };
 
 // attention segment sg of layer l of this step (an empty one has rem 0)
@@ -578,9 +579,9 @@ KIE_DI void cursor_attn_seg(const Dev& D, Cursor& c, int l, int sg) {
 
 KIE_DI void cursor_enter(const Dev& D, Cursor& c) {
   const KParams& p = *D.p;
-  const int lmph = 5 * p.m.L;
-  const int kind = c.ph == lmph ? PH_LM : phase_kind(p.m.parallel, c.ph % 5);
-  const int l = c.ph == lmph ? 0 : c.ph / 5;
+  int kind = PH_LM, l = 0;
+  if (c.ph < 5 * p.m.L) phase_at(p.lp.pipe, p.m.parallel, p.m.L, c.ph, &kind, &l);
+  c.layer = l;
   if (kind == PH_ATTN) {
     c.attn = 1;
     c.stride = (uint32_t)(attn_kpl(p.m.hd) * p.m.hd * 2);
@@ -606,7 +607,7 @@ KIE_DI void cursor_enter(const Dev& D, Cursor& c) {
 KIE_DI void cursor_advance(const Dev& D, Cursor& c) {
   while (c.rem == 0 && !c.done) {
     if (c.attn && c.seg == 0) {
-      cursor_attn_seg(D, c, c.ph / 5, 1);
+      cursor_attn_seg(D, c, c.layer, 1);
       continue;
     }
     if (++c.ph >= c.nph) {
@@ -1177,6 +1178,14 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
   // then issue no global loads (theirs would complete behind the ring loads
   // the waves have just issued).
   const bool early = PAR && G <= 2 && p.lp.hb >= 0;  // (four query heads per KV head: too many registers)
+  // pipelined phase order (set by the host only where early holds): the O
+  // prologue of layer l stages layer l + 2's input, which layer l + 2 reads
+  // after layer l + 1's phases
+  const int pipe = p.lp.pipe;
+  // x_{l+1+pipe} comes from the down projection of layer l + pipe - delay,
+  // which has run before the O prologue of layer l only for delay > pipe;
+  // otherwise each QKV polls its own input
+  const bool stage_x = p.m.delay > pipe;
   float* const hbs = lds_dyn + (early ? p.lp.hb : 0);
   uint16_t* const gst = (uint16_t*)(lds_dyn + (early ? p.lp.gst : 0));
   int* wgrows = D.desc + kWaves * kWaveDesc;
@@ -1213,6 +1222,7 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
   cur.ph = 0;
   cur.nph = 0;
   cur.done = 1;
+  cur.layer = 0;
   int slot = 0;
 
   int token = 0;
@@ -1295,8 +1305,8 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
     const int nph = nphases(p, s);
     for (int ph = 0; ph < nph; ++ph) {
       const bool is_lm = ph == 5 * L;
-      const int kind = is_lm ? PH_LM : phase_kind(PAR, ph % 5);
-      const int l = is_lm ? L : ph / 5;
+      int kind = PH_LM, l = L;
+      if (!is_lm) phase_at(pipe, PAR, L, ph, &kind, &l);
       const uint16_t* Wl = p.W + (uint64_t)(is_lm ? 0 : l) * p.pl.layer_stride;
 
       stamp(D, s, ph, 0);
@@ -1554,7 +1564,10 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
       // prologue: the input vector
       uint16_t gr[kGainRegs];
       float2 rope_cs = make_float2(1.f, 0.f);
-      const bool staged = early && l > 0 && !is_lm;  // input and gains fetched by the last O prologue
+      // gains (and, with a delay that publishes x in time, the input x)
+      // fetched by an O prologue
+      const bool staged = early && l > pipe && !is_lm;
+      const bool staged_x = staged && stage_x;
       if (kind == PH_QKV) {
         if (staged) {
           stashed_gains(D, gst, gr);
@@ -1572,7 +1585,7 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
           rope_cs = D.rope[(uint64_t)pos * (hd / 2) + i];
         }
         asm volatile("" ::: "memory");
-        if (!staged && (PAR ? (l > p.m.delay) : (l > 0))) {
+        if (!staged_x && (PAR ? (l > p.m.delay) : (l > 0))) {
           const int xi = PAR ? l : 2 * l;
           poll_to_lds<false>(D, D.X + (uint64_t)xi * d, xraw, d, epoch);
           wg_sync();
@@ -1614,19 +1627,22 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
         }
       } else if (kind == PH_O) {
         if (early) {
-          const bool next = l + 1 < L;
+          // the input of the next QKV of a layer above 0 (layer l + 1, or
+          // l + 2 in the pipelined order)
+          const int ln = l + 1 + pipe;
+          const bool next = ln < L;
           if (next) {
-            copy_halves(D, Wl + p.pl.layer_stride + p.pl.attn_norm, gst, d);
-            copy_halves(D, Wl + p.pl.layer_stride + p.pl.mlp_norm, gst + gains_pad(d), d);
+            copy_halves(D, Wl + (uint64_t)(1 + pipe) * p.pl.layer_stride + p.pl.attn_norm, gst, d);
+            copy_halves(D, Wl + (uint64_t)(1 + pipe) * p.pl.layer_stride + p.pl.mlp_norm, gst + gains_pad(d), d);
           }
           const bool want_hb = rfl(wgrows[2 * gemv_index(PH_DOWN) + 1]) > 0;
-          const bool want_x = next && l + 1 > p.m.delay;
+          const bool want_x = stage_x && next && ln > p.m.delay;
           // two round trips: down's input, then the next x and the
           // attention output together (when they fit the batches)
           const PollSeg s1[3] = {{D.HB + (uint64_t)l * F, hbs, want_hb ? F : 0, 1},
                                  {D.HB, hbs, 0, 1},
                                  {D.HB, hbs, 0, 1}};
-          const PollSeg s2[3] = {{D.X + (uint64_t)(l + 1) * d, xraw, want_x ? d : 0, 0},
+          const PollSeg s2[3] = {{D.X + (uint64_t)ln * d, xraw, want_x ? d : 0, 0},
                                  {D.OB + (uint64_t)l * qd, xs, qd, 1},
                                  {D.OB, xs, 0, 1}};
           if (s1[0].n <= kMultiPoll1 * kThreads) {

@@ -35,6 +35,40 @@ KIE_HD int phase_kind(int parallel, int j) {
                   : j;  // enum order is the sequential order
 }
 
+// The parallel block with a residual delay of two or more layers (and its
+// inputs staged in LDS, see LdsPlan::pipe) runs software-pipelined: layer
+// l's attention is followed by layer l + 1's QKV and gate/up, and only then
+// by layer l's O and down projections.
+//   QKV_0 GU_0 | ATTN_0 QKV_1 GU_1 O_0 DOWN_0 | ATTN_1 QKV_2 GU_2 O_1 DOWN_1
+//   | ... | ATTN_{L-1} O_{L-1} DOWN_{L-1}
+// x_{l+1} = x_l + P_{l-delay} is known once the down projection of layer
+// l - delay is done, so layer l + 1's QKV and gate/up need nothing from layer
+// l; the attention output then has two weight streams of slack before O
+// consumes it, and the QKV output three before attention does.  This is the
+// one-GPU form of the delayed all-reduce: a layer's partial sum is consumed
+// delay layers later, so its exchange hides under other layers' streams.
+// phase ph (0 <= ph < 5 L) of a step -> kind and layer
+KIE_HD void phase_at(int pipe, int parallel, int L, int ph, int* kind, int* layer) {
+  if (!pipe) {
+    *kind = phase_kind(parallel, ph % 5);
+    *layer = ph / 5;
+    return;
+  }
+  if (ph < 2) {
+    *kind = ph == 0 ? PH_QKV : PH_GU;
+    *layer = 0;
+    return;
+  }
+  const int j = (ph - 2) / 5 + 1, r = (ph - 2) % 5;  // super-step j = 1 .. L
+  if (j == L) {  // the last layer's tail: ATTN O DOWN
+    *kind = r == 0 ? PH_ATTN : r == 1 ? PH_O : PH_DOWN;
+    *layer = L - 1;
+    return;
+  }
+  *kind = r == 0 ? PH_ATTN : r == 1 ? PH_QKV : r == 2 ? PH_GU : r == 3 ? PH_O : PH_DOWN;
+  *layer = (r == 1 || r == 2) ? j : j - 1;
+}
+
 struct Dims {
   int L, d, H, Hkv, hd, F, V, G, max_ctx;
   int parallel, delay;
@@ -311,6 +345,12 @@ struct LdsPlan {
   // gains at half 0, MLP gains at half align(d, 512)), both fetched in
   // the O prologue; -1 when they do not fit
   int hb, gst;
+  // 1: the parallel block runs in the pipelined phase order (phase_at).  It
+  // needs the staged inputs above (two or fewer query heads per KV head) and
+  // a residual delay of at least two layers: the O prologue of layer l then
+  // stages x_{l+2}, which the down projection of layer l + 2 - delay - 1 <= l - 1
+  // has already published.
+  int pipe;
   int total_floats;
   int kmax, rmax, max_recs;
 };
@@ -359,6 +399,7 @@ KIE_HD LdsPlan lds_plan(const Dims& m, int nwg) {
   p.desc = o; o += kDescInts;
   p.hb = -1;
   p.gst = -1;
+  p.pipe = 0;
   if (m.parallel) {
     const int hb = (int)align_up((uint64_t)o, 64);
     const int gst = hb + kmax;
@@ -366,6 +407,7 @@ KIE_HD LdsPlan lds_plan(const Dims& m, int nwg) {
     if (end <= kMainFloats) {
       p.hb = hb;
       p.gst = gst;
+      p.pipe = m.G <= 2 && m.delay >= 2;
       o = end;
     }
   }

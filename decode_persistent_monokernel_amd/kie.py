@@ -80,6 +80,7 @@ def lib() -> C.CDLL:
         L.kie_launch_info.argtypes = [vp, C.POINTER(i32), C.POINTER(i32), C.POINTER(i32),
                                       C.POINTER(C.c_int64), C.POINTER(C.c_int64)]
         L.kie_validate_schedule.argtypes = [C.POINTER(ModelConfigC), i32, i32, C.c_char_p, sz]
+        L.kie_phase_order.argtypes = [C.POINTER(ModelConfigC), i32, C.POINTER(i32), C.POINTER(i32), i32]
         L.kie_position.argtypes = [vp]
         L.kie_position.restype = i32
         L.kie_status_string.argtypes = [C.c_int]
@@ -93,7 +94,7 @@ def lib() -> C.CDLL:
                      "kie_decode", "kie_set_position", "kie_sync_status",
                      "kie_set_timeout_us", "kie_set_debug_flags", "kie_set_sampling", "kie_set_launch_steps",
                      "kie_set_trace",
-                     "kie_pack_weights_host", "kie_launch_info", "kie_validate_schedule"):
+                     "kie_pack_weights_host", "kie_launch_info", "kie_validate_schedule", "kie_phase_order"):
             getattr(L, name).restype = C.c_int
         _lib = L
     return _lib
@@ -179,6 +180,19 @@ def validate_schedule(cfg: ModelConfig, n_workgroups: int, n_ctx: int) -> None:
     s = lib().kie_validate_schedule(C.byref(c), n_workgroups, n_ctx, buf, 256)
     if s != KIE_OK:
         raise KieError(s, buf.value.decode())
+
+
+PHASE_KIND_NAMES = ("QKV", "attention", "O", "gate/up", "down", "LM head")
+
+
+def phase_order(cfg: ModelConfig, n_workgroups: int) -> list:
+    """[(kind, layer)] of the phases of one decode step, in the kernel's
+    order (kind: 0 QKV, 1 attention, 2 O, 3 gate/up, 4 down, 5 LM head)"""
+    n = 5 * cfg.n_layers + 1
+    kind = (C.c_int32 * n)()
+    layer = (C.c_int32 * n)()
+    _check(lib().kie_phase_order(C.byref(config_c(cfg)), n_workgroups, kind, layer, n))
+    return list(zip(kind, layer))
 
 
 def create_status(cfg: ModelConfig, device: int = -1, max_ctx: Optional[int] = None) -> int:

@@ -257,6 +257,22 @@ kie_status kie_set_debug_flags(kie_ctx* ctx, uint32_t flags);
  * (steps*322*n_workgroups*32 bytes).  NULL / 0 turns tracing off. */
 kie_status kie_set_trace(kie_ctx* ctx, void* d_trace, int32_t steps);
 
+/* CPU-only: the phase order of one decode step for `cfg` on n_workgroups
+ * workgroups (the phase index of the trace above): phase p runs kind[p] of
+ * layer layer[p], kinds 0 QKV, 1 attention, 2 O, 3 gate/up, 4 down, 5 LM
+ * head (layer = n_layers).  The sequential block runs each layer's phases in
+ * that kind order.  The parallel block runs QKV, gate/up, attention, O, down
+ * per layer; with a residual delay of two or more layers (and two or fewer
+ * query heads per KV head) it is software-pipelined, layer l's attention
+ * followed by layer l + 1's QKV and gate/up before layer l's O and down: the
+ * delayed residual (the Laneformer lanes with Delayed Tensor Parallelism of
+ * the explainer pages' approach list) makes layer l + 1's input independent
+ * of layer l.  Writes 5 * n_layers + 1 entries;
+ * KIE_ERR_INVALID_ARG if n is smaller or the arrays are NULL,
+ * KIE_ERR_UNSUPPORTED for a shape the kernel does not run. */
+kie_status kie_phase_order(const kie_model_config* cfg, int32_t n_workgroups, int32_t* kind, int32_t* layer,
+                           int32_t n);
+
 /* Most decode steps one launch runs before the library starts the next one
  * (default 512); keeps each launch short. */
 kie_status kie_set_launch_steps(kie_ctx* ctx, int32_t steps);

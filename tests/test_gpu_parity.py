@@ -92,13 +92,20 @@ def test_small_shapes_teacher_forced(shape):
     eng.close()
 
 
-def test_lane_block_small():
-    cfg = CFG0.with_(name="lanes", n_layers=5, n_lanes=2, lane_delay=2, sequential=False, seed_index=12,
-                     prompt_len=7, decode_steps=10)
-    say("case parallel block, delay 2, 5 layers")
+@pytest.mark.parametrize("shape", [
+    # delay 2: the pipelined phase order (attention ahead of the next layer's QKV and gate/up)
+    dict(name="lanes-d2", n_layers=5, lane_delay=2, seed_index=12),
+    # delay 3 with two query heads per KV head: pipelined, GQA attention
+    dict(name="lanes-d3-gqa2", n_layers=6, lane_delay=3, n_kv_heads=2, seed_index=31),
+    # no delay: layer by layer, every QKV polls the x the down projection before it wrote
+    dict(name="lanes-d0", n_layers=4, lane_delay=0, seed_index=32),
+], ids=lambda s: s["name"])
+def test_lane_block_small(shape):
+    cfg = CFG0.with_(n_lanes=2, sequential=False, prompt_len=7, decode_steps=10, **shape)
+    say(f"case parallel block {shape}")
     w = gen_weights(cfg, overrides={"wq": 0.1, "wk": 0.1})
     rep, eng = teacher_forced(cfg, w, gen_prompt(cfg), cfg.decode_steps, make_engine, oracle_fp16_cache)
-    check(rep, "lanes-small")
+    check(rep, shape["name"])
     eng.close()
 
 
@@ -167,6 +174,8 @@ def test_deterministic_and_resumable():
     dict(name="mha", seed_index=17),
     dict(name="gqa4", n_heads=8, n_kv_heads=2, head_dim=32, seed_index=18),
     dict(name="lanes", n_layers=5, n_lanes=2, lane_delay=2, sequential=False, seed_index=19),
+    dict(name="lanes-d3-gqa2", n_layers=6, n_lanes=2, lane_delay=3, n_kv_heads=2, sequential=False, seed_index=33),
+    dict(name="lanes-d0", n_layers=4, n_lanes=2, lane_delay=0, sequential=False, seed_index=34),
 ], ids=lambda s: s["name"])
 def test_jitter_keeps_results_bitwise(shape):
     """race detection: with every wave sleeping a pseudo-random time at every

@@ -211,6 +211,54 @@ def test_schedule_covers_everything(cfg):
                 assert nwg != 256 and "LDS" in str(e), str(e)
 
 
+def _check_dependencies(cfg, order):
+    """producers before consumers, read off the block's equations: x_l is
+    x_0 for l <= delay (parallel block) and x_{l-1} + P_{l-delay-1} after,
+    published by that layer's down projection"""
+    L, par = cfg.n_layers, not cfg.sequential
+    pos = {(k, l): i for i, (k, l) in enumerate(order[:5 * L])}
+    assert len(pos) == 5 * L and order[-1] == (5, L)
+    Q, A, O, G, D = 0, 1, 2, 3, 4
+    for l in range(L):
+        src = (l - cfg.lane_delay - 1) if par else (l - 1)
+        for k in ((Q, G) if par else (Q,)):
+            if src >= 0:
+                assert pos[(D, src)] < pos[(k, l)]
+        assert pos[(Q, l)] < pos[(A, l)] < pos[(O, l)]
+        if not par:
+            assert pos[(O, l)] < pos[(G, l)]
+        assert pos[(G, l)] < pos[(D, l)] and pos[(O, l)] < pos[(D, l)]
+    return pos
+
+
+@needs_lib
+def test_phase_order():
+    """kie_phase_order: the sequential block runs layer by layer; the lane
+    block with a delay of two layers or more runs its attention ahead of the
+    next layer's QKV and gate/up, so two weight streams separate the
+    attention output from O; every order respects the block's dependencies"""
+    Q, A, O, G, D = 0, 1, 2, 3, 4
+    seq = kie.phase_order(CFG2, 256)
+    _check_dependencies(CFG2, seq)
+    assert [k for k, _ in seq[:10]] == [Q, A, O, G, D] * 2
+    pipe = kie.phase_order(CFG3, 256)
+    pos = _check_dependencies(CFG3, pipe)
+    assert [k for k, _ in pipe[:12]] == [Q, G, A, Q, G, O, D, A, Q, G, O, D]
+    assert [l for _, l in pipe[:12]] == [0, 0, 0, 1, 1, 0, 0, 1, 2, 2, 1, 1]
+    assert all(pos[(O, l)] - pos[(A, l)] == 3 for l in range(CFG3.n_layers - 1))
+    lanes = CFG0.with_(name="lanes", n_layers=6, n_lanes=2, sequential=False)
+    gqa4 = dict(n_heads=8, n_kv_heads=2, head_dim=32)  # four query heads per KV head: no staging
+    for delay, shape, piped in ((0, {}, False), (1, {}, False), (2, {}, True), (3, dict(n_kv_heads=2), True),
+                                (2, gqa4, False)):
+        cfg = lanes.with_(lane_delay=delay, **shape)
+        order = kie.phase_order(cfg, 256)
+        _check_dependencies(cfg, order)
+        assert ([k for k, _ in order[:4]] == [Q, G, A, Q]) == piped, (delay, kv)
+    assert kie.lib().kie_phase_order(None, 256, None, None, 0) != kie.KIE_OK
+    short = (C.c_int32 * 3)()
+    assert kie.lib().kie_phase_order(C.byref(kie.config_c(CFG3)), 256, short, short, 3) != kie.KIE_OK
+
+
 @needs_lib
 def test_schedule_validator_reports_problems():
     with pytest.raises(kie.KieError):
