@@ -102,7 +102,7 @@ def _rows(d, suffix):
         return list(csv.DictReader(fh))
 
 
-def summarize_trace(d: str, command: str) -> str:
+def summarize_trace(d: str, command: str, profiler_rc: int = 0) -> str:
     """markdown: per-kernel stats and every monokernel dispatch (for a trace of
     the --prefill mode: per-kernel stats and the batched prefill's share)"""
     stats = _rows(d, "kernel_stats.csv")
@@ -111,8 +111,13 @@ def summarize_trace(d: str, command: str) -> str:
     title = ("# rocprofv3 kernel trace of the batched prefill benchmark (cfg2, 2048-token prompt, chunks of 2048)"
              if prefill else
              "# rocprofv3 kernel trace of the default benchmark run (cfg2, 2048-token prompt, 512 decode steps)")
-    out = [title, "", "Command (from the repository root, on an MI355X):", "", "```", command, "```", "",
-           "| kernel | calls | total ms | average ms | min ms | max ms |", "|---|---|---|---|---|---|"]
+    out = [title, "", "Command (from the repository root, on an MI355X):", "", "```", command, "```", ""]
+    if profiler_rc:
+        out += [f"rocprofv3 exited with status {profiler_rc} after the program's last line and after the tool's "
+                "finalization had written every result file.  The same happens to any process that has both "
+                "torch's HIP runtime and this library's code object loaded (either alone exits 0 under the "
+                "profiler; plain runs exit 0); the figures below are complete.", ""]
+    out += ["| kernel | calls | total ms | average ms | min ms | max ms |", "|---|---|---|---|---|---|"]
     for r in stats:
         ns = lambda k: float(r[k]) / 1e6
         out.append(f"| `{r['Name'][:70]}` | {r['Calls']} | {ns('TotalDurationNs'):.3f} | {ns('AverageNs'):.3f} | "
@@ -136,11 +141,14 @@ def summarize_trace(d: str, command: str) -> str:
 
 
 def summarize_traffic(fetch_dir: str, write_dir: str, copy_bytes: int, cfg_name: str, steps: int,
-                      prompt: int) -> dict:
+                      prompt: int, ea_dir: str = "") -> dict:
     """HBM bytes of the timed decode launch from FETCH_SIZE / WRITE_SIZE (KiB
     per dispatch), each scaled by what it reads for a plain copy of
-    copy_bytes (read copy_bytes, write copy_bytes)"""
-    def pick(d, counter):
+    copy_bytes (read copy_bytes, write copy_bytes).  With ea_dir (a pass of
+    TCC_EA0_RDREQ_{32B,64B,128B}_sum and TCC_EA0_RDREQ_sum), also the read
+    bytes counted from the EA read requests by size, unscaled, for the kernel
+    and the copy: a second counter family for the read figure."""
+    def pick(d, counter, scale=1024.0):
         rows = [r for r in _rows(d, "counter_collection.csv") if r["Counter_Name"] == counter]
         mono = [r for r in rows if "kie_monokernel" in r["Kernel_Name"]]
         last_mono = max(int(r["Dispatch_Id"]) for r in mono) if mono else 0
@@ -149,12 +157,24 @@ def summarize_traffic(fetch_dir: str, write_dir: str, copy_bytes: int, cfg_name:
             raise SystemExit(f"{counter}: missing dispatches in {d}")
         timed = max(mono, key=lambda r: int(r["Dispatch_Id"]))
         copy = max(copies, key=lambda r: int(r["Dispatch_Id"]))  # the multiply that copies
-        return float(timed["Counter_Value"]) * 1024.0, float(copy["Counter_Value"]) * 1024.0, copy["Kernel_Name"]
+        return float(timed["Counter_Value"]) * scale, float(copy["Counter_Value"]) * scale, copy["Kernel_Name"]
     f_k, f_c, f_name = pick(fetch_dir, "FETCH_SIZE")
     w_k, w_c, _ = pick(write_dir, "WRITE_SIZE")
     sf, sw = copy_bytes / f_c, copy_bytes / w_c
     from decode_persistent_monokernel_amd.config import preset
     algo = preset(cfg_name).run_bytes(prompt, steps)
+    ea = {}
+    if ea_dir:
+        n = {k: pick(ea_dir, f"TCC_EA0_RDREQ{k}_sum", 1.0)[:2] for k in ("", "_32B", "_64B", "_128B")}
+        by_size = lambda i: 32 * n["_32B"][i] + 64 * n["_64B"][i] + 128 * n["_128B"][i]
+        ea = {
+            "ea_read_requests": {k or "all": n[k][0] for k in n},
+            "ea_read_bytes_per_launch": by_size(0),
+            "ea_read_bytes_copy": by_size(1),
+            "ea_copy_ratio": by_size(1) / copy_bytes,
+            "ea_read_ratio_to_fetch_scaled": by_size(0) / (f_k * sf),
+            "ea_unsized_requests": n[""][0] - n["_32B"][0] - n["_64B"][0] - n["_128B"][0],
+        }
     return {
         "config": cfg_name, "prompt": prompt, "decode_steps": steps,
         "kernel_source_hash": kernel_source_hash(),
@@ -165,6 +185,7 @@ def summarize_traffic(fetch_dir: str, write_dir: str, copy_bytes: int, cfg_name:
         "hbm_bytes_per_launch": f_k * sf + w_k * sw,
         "algorithmic_bytes_per_launch": algo,
         "ratio_to_algorithmic": (f_k * sf + w_k * sw) / algo,
+        **ea,
     }
 
 
@@ -280,10 +301,13 @@ def main():
                          "dispatch for scaling HBM counters)")
     ap.add_argument("--summarize-trace", metavar="DIR", help="write a markdown summary of a rocprofv3 "
                     "--kernel-trace --stats output directory to stdout and exit")
+    ap.add_argument("--ea-dir", default="", help="with --summarize-traffic: a rocprofv3 --pmc run of "
+                    "TCC_EA0_RDREQ_sum TCC_EA0_RDREQ_32B_sum TCC_EA0_RDREQ_64B_sum TCC_EA0_RDREQ_128B_sum")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="print the JSON traffic summary of two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) "
                          "of this command with --copy-bytes and exit")
     ap.add_argument("--command", default="", help="the profiled command, recorded in a summary")
+    ap.add_argument("--profiler-rc", type=int, default=0, help="rocprofv3's exit status, recorded in a summary")
     ap.add_argument("--launch-steps", type=int, default=0,
                     help="decode steps per kernel launch (default: all timed steps in one launch); 1 measures the "
                          "per-token launch cost the persistent kernel removes")
@@ -296,13 +320,13 @@ def main():
     args = ap.parse_args()
 
     if args.summarize_trace:
-        sys.stdout.write(summarize_trace(args.summarize_trace, args.command))
+        sys.stdout.write(summarize_trace(args.summarize_trace, args.command, args.profiler_rc))
         return
     if args.summarize_traffic:
         from decode_persistent_monokernel_amd.config import preset
         P = args.prompt if args.prompt is not None else preset(args.config).prompt_len
         res = summarize_traffic(args.summarize_traffic[0], args.summarize_traffic[1], args.copy_bytes,
-                                args.config, args.steps, P)
+                                args.config, args.steps, P, args.ea_dir)
         res["command"] = args.command
         print(json.dumps(res, indent=1))
         return
