@@ -1137,8 +1137,12 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
   Dev D;
   D.p = &P;
   D.tid = threadIdx.x;
-  D.wg = blockIdx.x;
   D.nwg = gridDim.x;
+  // The work partition numbers the workgroups XCD by XCD: the dispatcher
+  // places workgroup b on XCD b % 8, so index (b % 8) * (nwg / 8) + b / 8
+  // makes every contiguous range of the partition (a KV head's attention
+  // group and its merger, a stretch of GEMV rows) sit on one XCD.
+  D.wg = (D.nwg % 8 == 0) ? (int)(blockIdx.x % 8) * (D.nwg / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
   D.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   D.lane = threadIdx.x & 63;
   D.sh = &sh_static;
