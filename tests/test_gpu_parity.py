@@ -202,6 +202,44 @@ def test_jitter_keeps_results_bitwise(shape):
     eng.close()
 
 
+def random_shapes(n=12, seed=2024):
+    """n model shapes drawn from a fixed seed: 1-3 layers, d_model 128..1024
+    in steps of 8 (not only multiples of 64), head_dim 32..128 in steps of 8,
+    1, 2 or 4 query heads per KV head, FFN widths and vocabularies that are
+    not multiples of 256, the sequential block and the lane block with delay
+    0..3, prompts of 1..40 tokens; shapes the host does not run are redrawn"""
+    from decode_persistent_monokernel_amd import kie
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        G = (1, 2, 4)[len(out) % 3]
+        hkv = int(rng.integers(1, 5))
+        par = bool(rng.integers(0, 2))
+        cfg = CFG0.with_(
+            name=f"rand{len(out)}", n_layers=int(rng.integers(1, 4)), d_model=8 * int(rng.integers(16, 129)),
+            n_heads=G * hkv, n_kv_heads=hkv, head_dim=8 * int(rng.integers(4, 17)),
+            ffn_dim=8 * int(rng.integers(16, 385)), vocab=2 * int(rng.integers(250, 2501)),
+            sequential=not par, n_lanes=1, lane_delay=int(rng.integers(0, 4)) if par else 0,
+            prompt_len=int(rng.integers(1, 41)), decode_steps=6, seed_index=100 + len(out))
+        try:
+            kie.validate_schedule(cfg, 256, cfg.prompt_len + cfg.decode_steps + 1)
+        except kie.KieError:
+            continue
+        out.append(cfg)
+    return out
+
+
+@pytest.mark.parametrize("cfg", random_shapes(), ids=lambda c: c.name)
+def test_random_shapes_teacher_forced(cfg):
+    say(f"case random shape {cfg.name}: L{cfg.n_layers} d{cfg.d_model} H{cfg.n_heads}/{cfg.n_kv_heads}x"
+        f"{cfg.head_dim} F{cfg.ffn_dim} V{cfg.vocab} {'seq' if cfg.sequential else f'lanes d{cfg.lane_delay}'} "
+        f"P{cfg.prompt_len}")
+    w = gen_weights(cfg, overrides={"wq": 0.1, "wk": 0.1})
+    rep, eng = teacher_forced(cfg, w, gen_prompt(cfg), cfg.decode_steps, make_engine, oracle_fp16_cache)
+    check(rep, cfg.name)
+    eng.close()
+
+
 def test_bounded_wait_reports_timeout():
     """a workgroup waits on a word nobody writes: the launch must end with
     KIE_ERR_TIMEOUT, not hang, and the context must work again afterwards"""
