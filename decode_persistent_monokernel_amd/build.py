@@ -1,7 +1,8 @@
 """Compile the HIP library in-tree for gfx950.
 
-libkie.so = the persistent decode kernel (kie_kernel.hip) + the batched
-prefill kernels (kie_prefill.hip) + the host C ABI (kie_api.cpp).  Built with hipcc; packed fp32 vector instructions are turned
+libkie.so = the persistent decode kernel (kie_kernel.hip, built for two ring
+depths) + the batched prefill kernels (kie_prefill.hip) + the host C ABI
+(kie_api.cpp).  Built with hipcc; packed fp32 vector instructions are turned
 off for the device code (-packed-fp32-ops).
 """
 from __future__ import annotations
@@ -42,9 +43,12 @@ def build(verbose: bool = False) -> str:
     objs = []
     tmp = os.path.join(PKG, "_build")
     os.makedirs(tmp, exist_ok=True)
-    k_o = os.path.join(tmp, "kie_kernel.o")
-    _run([cc, f"--offload-arch={ARCH}", *common, *dev, "-c", os.path.join(CSRC, "kie_kernel.hip"), "-o", k_o], verbose)
-    objs.append(k_o)
+    # the decode kernel once per ring depth (kRingBase, kRingDeep in kie_layout.h)
+    for depth in (8, 10):
+        k_o = os.path.join(tmp, f"kie_kernel_ring{depth}.o")
+        _run([cc, f"--offload-arch={ARCH}", *common, *dev, f"-DKIE_RING_DEPTH={depth}", "-c",
+              os.path.join(CSRC, "kie_kernel.hip"), "-o", k_o], verbose)
+        objs.append(k_o)
     p_o = os.path.join(tmp, "kie_prefill.o")
     _run([cc, f"--offload-arch={ARCH}", *common, *dev, "-c", os.path.join(CSRC, "kie_prefill.hip"), "-o", p_o], verbose)
     objs.append(p_o)

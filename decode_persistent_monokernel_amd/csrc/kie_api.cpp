@@ -13,9 +13,13 @@
 #include "kie.h"
 #include "kie_layout.h"
 
-extern "C" hipError_t kie_internal_launch(const kie::KParams* kp, int nwg, size_t lds_bytes, hipStream_t stream);
-extern "C" hipError_t kie_internal_zero(void* p, size_t bytes, hipStream_t stream);
-extern "C" hipError_t kie_internal_occupancy(int G, int parallel, size_t lds_bytes, int* blocks_per_cu);
+// the decode kernel, built for each ring depth (kie_kernel.hip)
+extern "C" hipError_t kie_internal_launch_ring8(const kie::KParams* kp, int nwg, size_t lds_bytes, hipStream_t stream);
+extern "C" hipError_t kie_internal_launch_ring10(const kie::KParams* kp, int nwg, size_t lds_bytes, hipStream_t stream);
+extern "C" hipError_t kie_internal_zero_ring8(void* p, size_t bytes, hipStream_t stream);
+extern "C" hipError_t kie_internal_occupancy_ring8(int G, int parallel, size_t lds_bytes, int* blocks_per_cu);
+extern "C" hipError_t kie_internal_occupancy_ring10(int G, int parallel, size_t lds_bytes, int* blocks_per_cu);
+static_assert(kie::kRingBase == 8 && kie::kRingDeep == 10, "entry point names carry the ring depths");
 extern "C" hipError_t kie_internal_prefill_chunk(const kie::PrefillArgs* a, hipStream_t stream);
 extern "C" hipError_t kie_internal_noalloc_scratch(int device, void** ptr);
 
@@ -26,6 +30,7 @@ struct kie_ctx {
   int nwg = 256;
   kie::PackLayout pl;
   kie::WsLayout wl;
+  int depth = kie::kRingBase;  // ring slots per wave of the kernel this context runs
   kie::LdsPlan lp;
   void* packed = nullptr;
   void* kv = nullptr;
@@ -142,8 +147,9 @@ std::string check_supported(const kie::Dims& m, int nwg) {
   if (m.hd / 8 > 64) return "head_dim above 512 is not supported";
   if (m.d > kie::kGainRegs * kie::kThreads) return "d_model above 4096 is not supported";
   if (m.Hkv > nwg) return "more KV heads than workgroups";
-  const kie::LdsPlan lp = kie::lds_plan(m, nwg);
-  if (lp.total_floats > kie::kMainFloats) return "model needs more LDS than the kernel reserves";
+  const int budget = kie::main_floats(kie::ring_depth_for(m, nwg));
+  const kie::LdsPlan lp = kie::lds_plan(m, nwg, budget);
+  if (lp.total_floats > budget) return "model needs more LDS than the kernel reserves";
   const std::string po = check_phase_order(m, lp);
   if (!po.empty()) return po;
   const uint64_t lim = 0x7FFFFFFFull;
@@ -260,7 +266,8 @@ kie_status ready(kie_ctx* c) {
 kie_status launch(kie_ctx* c, kie::KParams& kp, hipStream_t st) {
   hipError_t e = hipSetDevice(c->device);
   if (e != hipSuccess) return hip_fail(c, e, "hipSetDevice");
-  e = kie_internal_launch(&kp, c->nwg, 0, st);
+  e = c->depth == kie::kRingDeep ? kie_internal_launch_ring10(&kp, c->nwg, 0, st)
+                                 : kie_internal_launch_ring8(&kp, c->nwg, 0, st);
   if (e != hipSuccess) return hip_fail(c, e, "monokernel launch");
   c->next_epoch += (uint32_t)kp.n_steps;
   return KIE_OK;
@@ -307,7 +314,9 @@ kie_status kie_create(const kie_model_config* cfg, int device, kie_ctx** out) {
   }
   if (device >= 0) {
     int per_cu = 0;
-    hipError_t e = kie_internal_occupancy(c->m.G, c->m.parallel, 0, &per_cu);
+    const int depth = kie::ring_depth_for(c->m, c->nwg);
+    hipError_t e = depth == kie::kRingDeep ? kie_internal_occupancy_ring10(c->m.G, c->m.parallel, 0, &per_cu)
+                                           : kie_internal_occupancy_ring8(c->m.G, c->m.parallel, 0, &per_cu);
     if (e != hipSuccess || per_cu < 1) {
       std::fprintf(stderr, "kie_create: kernel does not fit a compute unit (%s)\n",
                    e == hipSuccess ? "occupancy 0" : hipGetErrorString(e));
@@ -327,7 +336,8 @@ kie_status kie_create(const kie_model_config* cfg, int device, kie_ctx** out) {
   }
   c->pl = kie::pack_layout(c->m);
   c->wl = kie::ws_layout(c->m, c->nwg);
-  c->lp = kie::lds_plan(c->m, c->nwg);
+  c->depth = kie::ring_depth_for(c->m, c->nwg);
+  c->lp = kie::lds_plan(c->m, c->nwg, kie::main_floats(c->depth));
   *out = c;
   return KIE_OK;
 }
@@ -357,8 +367,8 @@ kie_status kie_bind_memory(kie_ctx* c, void* d_packed, void* d_kv, void* d_ws) {
   c->next_epoch = 1;
   // clear state and exchange words, upload the RoPE table
   uint8_t* w = (uint8_t*)d_ws;
-  if ((e = kie_internal_zero(w + c->wl.state, 256, nullptr)) != hipSuccess) return hip_fail(c, e, "clear state");
-  if ((e = kie_internal_zero(w + c->wl.ll_begin, c->wl.ll_end - c->wl.ll_begin, nullptr)) != hipSuccess)
+  if ((e = kie_internal_zero_ring8(w + c->wl.state, 256, nullptr)) != hipSuccess) return hip_fail(c, e, "clear state");
+  if ((e = kie_internal_zero_ring8(w + c->wl.ll_begin, c->wl.ll_end - c->wl.ll_begin, nullptr)) != hipSuccess)
     return hip_fail(c, e, "clear exchange words");
   std::vector<float> rope;
   rope_table(c->m, c->cfg.rope_base, rope);
@@ -537,7 +547,7 @@ kie_status kie_sync_status(kie_ctx* c, void* stream) {
   if (e != hipSuccess) return hip_fail(c, e, "clear status");
   // an aborted launch leaves exchange words and arrival counters part-way
   // through a step: start the exchange state over (the KV cache is kept)
-  e = kie_internal_zero((uint8_t*)c->ws + c->wl.ll_begin, c->wl.ll_end - c->wl.ll_begin, nullptr);
+  e = kie_internal_zero_ring8((uint8_t*)c->ws + c->wl.ll_begin, c->wl.ll_end - c->wl.ll_begin, nullptr);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) return hip_fail(c, e, "reset exchange state");
   c->next_epoch = 1;
@@ -580,7 +590,7 @@ kie_status kie_phase_order(const kie_model_config* cfg, int32_t nwg, int32_t* ki
   const kie::Dims m = make_dims(*cfg);
   if (n < 5 * m.L + 1) return KIE_ERR_INVALID_ARG;
   if (!check_supported(m, nwg).empty()) return KIE_ERR_UNSUPPORTED;
-  const kie::LdsPlan lp = kie::lds_plan(m, nwg);
+  const kie::LdsPlan lp = kie::lds_plan(m, nwg, kie::main_floats(kie::ring_depth_for(m, nwg)));
   for (int ph = 0; ph < 5 * m.L; ++ph) {
     int k, l;
     kie::phase_at(lp.pipe, m.parallel, m.L, ph, &k, &l);
@@ -615,7 +625,7 @@ kie_status kie_launch_info(const kie_ctx* c, int32_t* nwg, int32_t* threads, int
   if (!c) return KIE_ERR_INVALID_ARG;
   if (nwg) *nwg = c->nwg;
   if (threads) *threads = kie::kThreads;
-  if (lds) *lds = kie::kMainFloats * 4 + kie::kWaves * kie::kRingDepth * 1024;
+  if (lds) *lds = kie::main_floats(c->depth) * 4 + kie::kWaves * c->depth * 1024;
   if (qkv_off) *qkv_off = (int64_t)c->pl.wqkv;
   if (lm_off) *lm_off = (int64_t)c->pl.lm_head;
   return KIE_OK;
@@ -694,7 +704,7 @@ kie_status kie_validate_schedule(const kie_model_config* cfg, int32_t nwg, int32
   }
   for (int v : key_owner)
     if (v != 1) return bad("attention key covered zero or several times");
-  const kie::LdsPlan lp = kie::lds_plan(m, nwg);
+  const kie::LdsPlan lp = kie::lds_plan(m, nwg, kie::main_floats(kie::ring_depth_for(m, nwg)));
   // every workgroup's GEMV rows fit the LDS partial sums (and, in the
   // parallel block, the kept O and residual rows)
   for (int k : kinds) {

@@ -31,7 +31,16 @@
 
 #include "kie_layout.h"
 
+// This file is compiled once per ring depth (KIE_RING_DEPTH, see
+// kie_layout.h): each build's code lives in its own namespace and its entry
+// points carry the depth in their names.
+#define KIE_CAT2(a, b) a##b
+#define KIE_CAT(a, b) KIE_CAT2(a, b)
+#define KIE_RING_NS KIE_CAT(ring, KIE_RING_DEPTH)
+#define KIE_RING_ENTRY(name) KIE_CAT(KIE_CAT(name, _ring), KIE_RING_DEPTH)
+
 namespace kie {
+namespace KIE_RING_NS {
 
 typedef unsigned long long u64;
 constexpr int kDepth = kRingDepth;  // 1-KB wave units in flight per wave (LDS ring slots)
@@ -1915,6 +1924,7 @@ __global__ void kie_zero_kernel(uint4* p, uint64_t n16) {
     p[i] = make_uint4(0, 0, 0, 0);
 }
 
+}  // namespace KIE_RING_NS
 }  // namespace kie
 
 // ---------------------------------------------------------------------------
@@ -1925,17 +1935,18 @@ __global__ void kie_zero_kernel(uint4* p, uint64_t n16) {
 // other's branches
 static const void* kie_kernel_for(int G, int parallel) {
   switch (G * 2 + (parallel ? 1 : 0)) {
-    case 2: return (const void*)&kie::kie_monokernel<1, false>;
-    case 3: return (const void*)&kie::kie_monokernel<1, true>;
-    case 4: return (const void*)&kie::kie_monokernel<2, false>;
-    case 5: return (const void*)&kie::kie_monokernel<2, true>;
-    case 8: return (const void*)&kie::kie_monokernel<4, false>;
-    case 9: return (const void*)&kie::kie_monokernel<4, true>;
+    case 2: return (const void*)&kie::KIE_RING_NS::kie_monokernel<1, false>;
+    case 3: return (const void*)&kie::KIE_RING_NS::kie_monokernel<1, true>;
+    case 4: return (const void*)&kie::KIE_RING_NS::kie_monokernel<2, false>;
+    case 5: return (const void*)&kie::KIE_RING_NS::kie_monokernel<2, true>;
+    case 8: return (const void*)&kie::KIE_RING_NS::kie_monokernel<4, false>;
+    case 9: return (const void*)&kie::KIE_RING_NS::kie_monokernel<4, true>;
     default: return nullptr;
   }
 }
 
-extern "C" hipError_t kie_internal_launch(const kie::KParams* kp, int nwg, size_t lds_bytes, hipStream_t stream) {
+extern "C" hipError_t KIE_RING_ENTRY(kie_internal_launch)(const kie::KParams* kp, int nwg, size_t lds_bytes,
+                                                          hipStream_t stream) {
   const void* fn = kie_kernel_for(kp->m.G, kp->m.parallel);
   if (!fn) return hipErrorInvalidValue;
   (void)lds_bytes;  // all LDS is static
@@ -1943,17 +1954,18 @@ extern "C" hipError_t kie_internal_launch(const kie::KParams* kp, int nwg, size_
   return hipLaunchCooperativeKernel(fn, dim3(nwg), dim3(kie::kThreads), args, 0, stream);
 }
 
-extern "C" hipError_t kie_internal_zero(void* p, size_t bytes, hipStream_t stream) {
+extern "C" hipError_t KIE_RING_ENTRY(kie_internal_zero)(void* p, size_t bytes, hipStream_t stream) {
   if (bytes == 0) return hipSuccess;
   if (((uintptr_t)p & 15) || (bytes & 15)) return hipErrorInvalidValue;
   const uint64_t n16 = bytes / 16;
   const uint64_t want = (n16 + 255) / 256;
   const int blocks = (int)(want < 4096 ? want : 4096);
-  hipLaunchKernelGGL(kie::kie_zero_kernel, dim3(blocks), dim3(256), 0, stream, (uint4*)p, n16);
+  hipLaunchKernelGGL(kie::KIE_RING_NS::kie_zero_kernel, dim3(blocks), dim3(256), 0, stream, (uint4*)p, n16);
   return hipGetLastError();
 }
 
-extern "C" hipError_t kie_internal_occupancy(int G, int parallel, size_t lds_bytes, int* blocks_per_cu) {
+extern "C" hipError_t KIE_RING_ENTRY(kie_internal_occupancy)(int G, int parallel, size_t lds_bytes,
+                                                             int* blocks_per_cu) {
   const void* fn = kie_kernel_for(G, parallel);
   if (!fn) return hipErrorInvalidValue;
   (void)lds_bytes;

@@ -321,10 +321,17 @@ KIE_HD int attn_kpl(int hd) { return kWave / (hd / 8); }
 constexpr int kWaveDesc = 64;
 constexpr int kConsumerAttn = 52;
 constexpr int kDescInts = kWaves * kWaveDesc + 16;
+// The library holds the kernel built for two ring depths (LDS slots per
+// wave): kRingDeep for the sequential block wherever its LDS plan fits
+// beside the deeper ring (more of the next phases' weights in flight while
+// a wave waits on an exchange: cfg1 -3.8 %, cfg2 -0.4 % per token), and
+// kRingBase otherwise.  The lane block keeps the base ring: a deeper one
+// leaves no LDS for its staged inputs.
+constexpr int kRingBase = 8, kRingDeep = 10;
 #ifndef KIE_RING_DEPTH
 #define KIE_RING_DEPTH 8
 #endif
-constexpr int kRingDepth = KIE_RING_DEPTH;
+constexpr int kRingDepth = KIE_RING_DEPTH;  // the depth of the kernel being compiled
 // LDS of one workgroup: the ring (kWaves x depth KB), a small block of
 // shared scalars, and one static array of main_floats(depth) floats for
 // everything else; a model whose LdsPlan needs more is rejected by the host
@@ -355,7 +362,8 @@ struct LdsPlan {
   int kmax, rmax, max_recs;
 };
 KIE_HD int imax(int a, int b) { return a > b ? a : b; }
-KIE_HD LdsPlan lds_plan(const Dims& m, int nwg) {
+// the plan for a kernel whose main LDS array holds `budget` floats
+KIE_HD LdsPlan lds_plan(const Dims& m, int nwg, int budget) {
   LdsPlan p{};
   // GEMV input: two planes of kmax/2 floats (elements 8g..8g+3 at plane 0,
   // 8g+4..8g+7 at plane 1, position 4g), covering padded_cols(K) elements
@@ -404,7 +412,7 @@ KIE_HD LdsPlan lds_plan(const Dims& m, int nwg) {
     const int hb = (int)align_up((uint64_t)o, 64);
     const int gst = hb + kmax;
     const int end = gst + (int)align_up((uint64_t)m.d, kBlock);  // 2 x align(d, 512) halves
-    if (end <= kMainFloats) {
+    if (end <= budget) {
       p.hb = hb;
       p.gst = gst;
       p.pipe = m.G <= 2 && m.delay >= 2;
@@ -414,12 +422,19 @@ KIE_HD LdsPlan lds_plan(const Dims& m, int nwg) {
   // phase trace of one step (32-bit stamps, written out at the step's end),
   // when it fits; otherwise stamps go straight to memory
   p.trace = -1;
-  if (o + trace_slots(m.L) * 4 <= kMainFloats) {
+  if (o + trace_slots(m.L) * 4 <= budget) {
     p.trace = o;
     o += trace_slots(m.L) * 4;
   }
   p.total_floats = o;
   return p;
+}
+
+// the ring depth the host runs a model with (kRingDeep or kRingBase)
+KIE_HD int ring_depth_for(const Dims& m, int nwg) {
+  if (m.parallel) return kRingBase;
+  const int deep = main_floats(kRingDeep);
+  return lds_plan(m, nwg, deep).total_floats <= deep ? kRingDeep : kRingBase;
 }
 
 // arguments of one monokernel launch

@@ -282,8 +282,10 @@ kie_status kie_set_launch_steps(kie_ctx* ctx, int32_t steps);
 kie_status kie_pack_weights_host(const kie_model_config* cfg, const kie_weights* src, void* host_dst);
 
 /* Launch shape: workgroups (= compute units), threads per workgroup, LDS
- * bytes per workgroup, KV-cache positions per wave load, and the packed
- * element offsets of layer 0's fused QKV matrix and the LM head. */
+ * bytes per workgroup (the same 160 KB whichever ring depth the context
+ * runs: 10 one-KB slots per wave for the sequential block when its LDS plan
+ * fits beside them, 8 otherwise), and the packed element offsets of layer
+ * 0's fused QKV matrix and the LM head. */
 kie_status kie_launch_info(const kie_ctx* ctx, int32_t* n_workgroups, int32_t* threads, int32_t* lds_bytes,
                            int64_t* qkv_offset, int64_t* lm_offset);
 
