@@ -339,6 +339,7 @@ def main():
     import torch
     from decode_persistent_monokernel_amd.config import preset
     from decode_persistent_monokernel_amd.inputs import gen_weights, gen_prompt
+    from decode_persistent_monokernel_amd import kie
     from decode_persistent_monokernel_amd.kie import Engine
 
     cfg = preset(args.config)
@@ -428,8 +429,7 @@ def main():
             "algorithmic_bytes_per_launch": algo_bytes,
             "kernel_ms": round(kernel_ms, 3),
             "launch_ms_all": [round(x, 3) for x in launch_ms],
-            "kernel": f"kie::kie_monokernel<{cfg.n_heads // cfg.n_kv_heads}, "
-                      f"{'false' if cfg.sequential else 'true'}>",
+            "kernel": kie.kernel_name(cfg, eng.launch_info()["n_workgroups"]),
         },
         "tokens_head": [int(t) for t in toks[:8]],
     }

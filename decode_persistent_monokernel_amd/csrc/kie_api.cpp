@@ -602,6 +602,14 @@ kie_status kie_phase_order(const kie_model_config* cfg, int32_t nwg, int32_t* ki
   return KIE_OK;
 }
 
+kie_status kie_ring_depth(const kie_model_config* cfg, int32_t nwg, int32_t* depth) {
+  if (!cfg || nwg <= 0 || !depth || !check_config(*cfg).empty()) return KIE_ERR_INVALID_ARG;
+  const kie::Dims m = make_dims(*cfg);
+  if (!check_supported(m, nwg).empty()) return KIE_ERR_UNSUPPORTED;
+  *depth = kie::ring_depth_for(m, nwg);
+  return KIE_OK;
+}
+
 kie_status kie_set_launch_steps(kie_ctx* c, int32_t steps) {
   if (!c || steps <= 0) return KIE_ERR_INVALID_ARG;
   c->launch_steps = steps;

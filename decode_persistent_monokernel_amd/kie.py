@@ -81,6 +81,7 @@ def lib() -> C.CDLL:
                                       C.POINTER(C.c_int64), C.POINTER(C.c_int64)]
         L.kie_validate_schedule.argtypes = [C.POINTER(ModelConfigC), i32, i32, C.c_char_p, sz]
         L.kie_phase_order.argtypes = [C.POINTER(ModelConfigC), i32, C.POINTER(i32), C.POINTER(i32), i32]
+        L.kie_ring_depth.argtypes = [C.POINTER(ModelConfigC), i32, C.POINTER(i32)]
         L.kie_position.argtypes = [vp]
         L.kie_position.restype = i32
         L.kie_status_string.argtypes = [C.c_int]
@@ -94,7 +95,8 @@ def lib() -> C.CDLL:
                      "kie_decode", "kie_set_position", "kie_sync_status",
                      "kie_set_timeout_us", "kie_set_debug_flags", "kie_set_sampling", "kie_set_launch_steps",
                      "kie_set_trace",
-                     "kie_pack_weights_host", "kie_launch_info", "kie_validate_schedule", "kie_phase_order"):
+                     "kie_pack_weights_host", "kie_launch_info", "kie_validate_schedule", "kie_phase_order",
+                     "kie_ring_depth"):
             getattr(L, name).restype = C.c_int
         _lib = L
     return _lib
@@ -193,6 +195,21 @@ def phase_order(cfg: ModelConfig, n_workgroups: int) -> list:
     layer = (C.c_int32 * n)()
     _check(lib().kie_phase_order(C.byref(config_c(cfg)), n_workgroups, kind, layer, n))
     return list(zip(kind, layer))
+
+
+def ring_depth(cfg: ModelConfig, n_workgroups: int) -> int:
+    """LDS ring slots per wave of the decode kernel build a context for cfg
+    on n_workgroups workgroups launches (8 or 10)"""
+    d = C.c_int32()
+    _check(lib().kie_ring_depth(C.byref(config_c(cfg)), n_workgroups, C.byref(d)))
+    return d.value
+
+
+def kernel_name(cfg: ModelConfig, n_workgroups: int) -> str:
+    """the decode kernel's symbol as profilers print it"""
+    g = cfg.n_heads // cfg.n_kv_heads
+    par = "false" if cfg.sequential else "true"
+    return f"kie::ring{ring_depth(cfg, n_workgroups)}::kie_monokernel<{g}, {par}>"
 
 
 def create_status(cfg: ModelConfig, device: int = -1, max_ctx: Optional[int] = None) -> int:

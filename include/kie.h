@@ -273,6 +273,17 @@ kie_status kie_set_trace(kie_ctx* ctx, void* d_trace, int32_t steps);
 kie_status kie_phase_order(const kie_model_config* cfg, int32_t n_workgroups, int32_t* kind, int32_t* layer,
                            int32_t n);
 
+/* CPU-only: ring slots per wave (*depth, 8 or 10) of the decode kernel build
+ * that a context for `cfg` on n_workgroups workgroups launches.  Each wave
+ * streams its weight chunks through a ring of one-KB LDS slots (the weights
+ * stream through on-chip memory once per token, as the monokernel pages
+ * describe the weight path); the deeper ring is used for the sequential block
+ * when its other LDS buffers fit beside it.  The two builds are the same
+ * kernel, named kie::ring8:: and kie::ring10:: in profiler output.
+ * KIE_ERR_INVALID_ARG for a bad config or NULL depth, KIE_ERR_UNSUPPORTED
+ * for a shape the kernel does not run. */
+kie_status kie_ring_depth(const kie_model_config* cfg, int32_t n_workgroups, int32_t* depth);
+
 /* Most decode steps one launch runs before the library starts the next one
  * (default 512); keeps each launch short. */
 kie_status kie_set_launch_steps(kie_ctx* ctx, int32_t steps);

@@ -253,10 +253,25 @@ def test_phase_order():
         cfg = lanes.with_(lane_delay=delay, **shape)
         order = kie.phase_order(cfg, 256)
         _check_dependencies(cfg, order)
-        assert ([k for k, _ in order[:4]] == [Q, G, A, Q]) == piped, (delay, kv)
+        assert ([k for k, _ in order[:4]] == [Q, G, A, Q]) == piped, (delay, shape)
     assert kie.lib().kie_phase_order(None, 256, None, None, 0) != kie.KIE_OK
     short = (C.c_int32 * 3)()
     assert kie.lib().kie_phase_order(C.byref(kie.config_c(CFG3)), 256, short, short, 3) != kie.KIE_OK
+
+
+@needs_lib
+def test_ring_depth():
+    """kie_ring_depth: the sequential block runs ten LDS slots per wave when
+    its other LDS buffers fit beside them, the lane block and the 8B shape's
+    larger buffers keep eight; the kernel name carries the depth"""
+    assert [kie.ring_depth(c, 256) for c in (CFG0, CFG1, CFG2, CFG3, CFG4)] == [10, 10, 10, 8, 8]
+    assert kie.kernel_name(CFG2, 256) == "kie::ring10::kie_monokernel<1, false>"
+    assert kie.kernel_name(CFG3, 256) == "kie::ring8::kie_monokernel<1, true>"
+    assert kie.kernel_name(CFG4, 256) == "kie::ring8::kie_monokernel<4, false>"
+    d = C.c_int32()
+    assert kie.lib().kie_ring_depth(C.byref(kie.config_c(CFG2)), 256, None) == -1  # KIE_ERR_INVALID_ARG
+    assert kie.lib().kie_ring_depth(None, 256, C.byref(d)) == -1  # KIE_ERR_INVALID_ARG
+    assert kie.lib().kie_ring_depth(C.byref(kie.config_c(CFG2)), 0, C.byref(d)) == -1  # KIE_ERR_INVALID_ARG
 
 
 @needs_lib
