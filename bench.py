@@ -313,7 +313,7 @@ def main():
                          "per-token launch cost the persistent kernel removes")
     ap.add_argument("--phase-trace", metavar="FILE", default="",
                     help="after the timed run, trace 16 decode steps and write the per-phase critical-path "
-                         "summary (markdown) to FILE")
+                         "summary (markdown) to FILE, and the raw stamps to FILE's stem + _stamps.npz")
     ap.add_argument("--prefill", action="store_true",
                     help="instead of the decode benchmark, time the batched prefill of the prompt and print "
                          "its own JSON line (matrix-core roofline)")
@@ -446,6 +446,9 @@ def main():
         cmd = "python bench.py " + " ".join(a for a in sys.argv[1:])
         with open(args.phase_trace, "w") as fh:
             fh.write(phase_trace_summary(tr, cfg, wall * 1e3 / K, cmd))
+        # the raw stamps beside the summary, for analyses of their own
+        np.savez_compressed(os.path.splitext(args.phase_trace)[0] + "_stamps.npz", stamps=tr,
+                            order=np.array(kie.phase_order(cfg, tr.shape[2]), dtype=np.int32))
     # release every device buffer while the runtime (and a profiler attached
     # to it) is still fully up: nothing is left for interpreter teardown
     del out
