@@ -940,11 +940,89 @@ KIE_DI void attn_step2_full(const Dev& D, const u4v k0, const u4v v0, const u4v 
   }
 }
 
+// attn_step2_full with the key's lane count LPK fixed at compile time
+// (0: the run-time width), for the heads-per-KV-head counts whose key loop
+// is bound by vector instructions
+template <int LPK>
+KIE_DI float group_sum_t(const Dev& D, float v) {
+  if constexpr (LPK == 16) {
+    return row16_sum(v);
+  } else {
+    return group_sum(v, D.lpk, D.dl);
+  }
+}
+template <int G, int LPK>
+KIE_DI void attn_step2_full_t(const Dev& D, const u4v k0, const u4v v0, const u4v k1, const u4v v1,
+                              const float (&q)[G][8], float (&mrow)[G], float (&lrow)[G], float (&acc)[G][8]) {
+  const uint32_t vw0[4] = {v0.x, v0.y, v0.z, v0.w}, vw1[4] = {v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float t0 = dot_chunk(k0, f4v{q[h][0], q[h][1], q[h][2], q[h][3]}, f4v{q[h][4], q[h][5], q[h][6], q[h][7]});
+    float t1 = dot_chunk(k1, f4v{q[h][0], q[h][1], q[h][2], q[h][3]}, f4v{q[h][4], q[h][5], q[h][6], q[h][7]});
+    t0 = group_sum_t<LPK>(D, t0);
+    t1 = group_sum_t<LPK>(D, t1);
+    const float mn = fmaxf(mrow[h], fmaxf(t0, t1));
+    const float sc = __builtin_amdgcn_exp2f(mrow[h] - mn);
+    const float p0 = __builtin_amdgcn_exp2f(t0 - mn);
+    const float p1 = __builtin_amdgcn_exp2f(t1 - mn);
+    lrow[h] = __builtin_fmaf(lrow[h], sc, p0 + p1);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc[h][2 * j] = __builtin_fmaf(p1, h2f_lo(vw1[j]), __builtin_fmaf(p0, h2f_lo(vw0[j]), acc[h][2 * j] * sc));
+      acc[h][2 * j + 1] =
+          __builtin_fmaf(p1, h2f_hi(vw1[j]), __builtin_fmaf(p0, h2f_hi(vw0[j]), acc[h][2 * j + 1] * sc));
+    }
+    mrow[h] = mn;
+  }
+}
+// the whole pairs of key steps [st, nfull) of a segment, all inside the
+// context, through attn_step2_full_t (see attn_stream)
+template <int G, int LPK>
+KIE_DI void attn_pairs_full(const Dev& D, Cursor& cur, int& slot, Owed& owed, int& st, int nfull,
+                            const float (&q)[G][8], float (&mrow)[G], float (&lrow)[G], float (&acc)[G][8]) {
+  for (; st < nfull; st += 2) {
+    uint32_t ra[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) ra[k] = ring_addr(D, ring_add(slot, k));
+    if (rfl(owed.n) == 0) {
+      __builtin_amdgcn_s_waitcnt(kWaitRing4);
+    } else {
+      __builtin_amdgcn_s_waitcnt(kWaitAllVm);
+    }
+    u4v x[4];
+    read_kv2(ra, x);
+    if (owed.n == 0 && cur.attn && !cur.done && cur.rem >= 4 && cur.kvh == 0) {
+      cursor_issue4(D, cur, slot);
+    } else {
+      attn_refill(D, cur, slot, 4, owed);
+    }
+    slot = ring_add(slot, 4);
+    attn_step2_full_t<G, LPK>(D, x[0], x[1], x[2], x[3], q, mrow, lrow, acc);
+  }
+}
+
 template <int G>
 KIE_DI void attn_stream(const Dev& D, Cursor& cur, int& slot, Owed& owed, int nst, int ka, int kc,
                         const float (&q)[G][8], float (&mrow)[G], float (&lrow)[G], float (&acc)[G][8]) {
   make_uniform(cur, slot);
   int st = 0;
+  if constexpr (G > 2) {
+    // More than two query heads per KV head: the pairs of key steps that lie
+    // wholly inside the context go first, through the fused two-key update,
+    // then the rest (the loop below).  One loop body holding both forms
+    // needs more registers than the kernel has; per key, the separate
+    // update costs about twice the vector instructions, which made the
+    // attention of four query heads per KV head arithmetic-bound.  The
+    // key's lane count is fixed per loop (16 lanes for head_dim 128), so
+    // the per-key sums carry no width dispatch.
+    const int nk = (kc - ka) / D.kpl;  // key steps wholly inside the context
+    const int nfull = rfl(imax(0, nk < nst ? nk : nst) & ~1);
+    if (D.lpk == 16) {
+      attn_pairs_full<G, 16>(D, cur, slot, owed, st, nfull, q, mrow, lrow, acc);
+    } else {
+      attn_pairs_full<G, 0>(D, cur, slot, owed, st, nfull, q, mrow, lrow, acc);
+    }
+  }
   for (; st + 2 <= nst; st += 2) {
     uint32_t ra[4];
 #pragma unroll
