@@ -1001,6 +1001,76 @@ KIE_DI void attn_pairs_full(const Dev& D, Cursor& cur, int& slot, Owed& owed, in
   }
 }
 
+// A merger's poll of its group's records into LDS (record r, head h at
+// recs[(r * G + h) * (hd + 2) ...]) with K words per thread per round
+// trip, for more than two query heads per KV head: those records hold G
+// heads each, and in batches of eight words a 32-record group takes five
+// round trips one after the other.  Word offsets are kept as 32 bits from
+// the record buffer.  A missing record reads as empty (m = -inf); on abort
+// or time-out the loop stops (the caller checks after its barrier).
+template <int K>
+KIE_DI void merger_poll_wide(const Dev& D, int l, int w_first, int nrec, int rw, int hd, const float* mlw,
+                             float* recs, uint32_t epoch) {
+  const int n = nrec * rw;
+  for (int base = D.tid; base < n; base += kThreads * K) {
+    uint32_t off[K];
+    uint32_t mask = 0;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int i = base + k * kThreads;
+      off[k] = 0;
+      if (i < n) {
+        const int r = i / rw, o = i % rw;
+        const int si = (int)mlw[r * 8 + 7];
+        if (si >= 0) {
+          off[k] = (uint32_t)((((uint64_t)l * D.nwg + w_first + r) * 2 + si) * rw + o);
+          mask |= 1u << k;
+        }
+      }
+    }
+    u64 vv[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+      if (mask & (1u << k)) vv[k] = ll_load(D.REC + off[k]);
+    const uint64_t t0 = wall_clock64();
+    for (int it = 0;; ++it) {
+      uint32_t stale = 0;
+#pragma unroll
+      for (int k = 0; k < K; ++k)
+        if ((mask & (1u << k)) && ll_epoch(vv[k]) != epoch) stale |= 1u << k;
+      if (!stale) break;
+      if ((it & 15) == 15) {
+        if (abort_seen(D)) break;
+        if (__hip_atomic_load(&D.state[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) {
+          set_abort(D);
+          break;
+        }
+        if (wall_clock64() - t0 > D.p->timeout_ticks) {
+          raise_status(D, DEV_TIMEOUT);
+          break;
+        }
+      }
+      __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+      for (int k = 0; k < K; ++k)
+        if (stale & (1u << k)) vv[k] = ll_load(D.REC + off[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const int i = base + k * kThreads;
+      if (i < n) {
+        float v = 0.f;
+        if (mask & (1u << k)) {
+          v = ll_f(vv[k]);
+        } else if ((i % rw) % (hd + 2) == 0) {
+          v = -INFINITY;  // missing record: empty
+        }
+        recs[i] = v;
+      }
+    }
+  }
+}
+
 template <int G>
 KIE_DI void attn_stream(const Dev& D, Cursor& cur, int& slot, Owed& owed, int nst, int ka, int kc,
                         const float (&q)[G][8], float (&mrow)[G], float (&lrow)[G], float (&acc)[G][8]) {
@@ -1552,6 +1622,9 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
           //    (record r, head h at recs[(r*G + h)*(hd+2) ...])
           float* recs = wrec;  // the wave records are consumed already
           const int rw = G * (hd + 2);
+          if constexpr (G > 2) {
+            merger_poll_wide<17>(D, l, w_first, nrec, rw, hd, mlw, recs, epoch);
+          } else {
           for (int base = D.tid; base < nrec * rw; base += kThreads * 8) {
             u64 vv[8];
             uint32_t mask = 0;
@@ -1609,6 +1682,7 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
                 recs[i] = v;
               }
             }
+          }
           }
           wg_sync();
           if (aborted(D)) { __builtin_amdgcn_s_waitcnt(kWaitAllVm); return; }
