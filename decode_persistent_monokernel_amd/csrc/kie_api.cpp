@@ -657,7 +657,7 @@ kie_status kie_validate_schedule(const kie_model_config* cfg, int32_t nwg, int32
     std::vector<int> owner(sh.rows, -1);
     for (int w = 0; w < nwg; ++w) {
       int r0, r1;
-      kie::gemv_rows(m, k, nwg, w, &r0, &r1);
+      kie::gemv_rows_any(m, k, nwg, w, &r0, &r1);
       if (r0 % sh.unit_rows || r1 % sh.unit_rows) return bad("row range splits a row group");
       for (int r = r0; r < r1; ++r) {
         if (r < 0 || r >= sh.rows || owner[r] != -1) return bad("GEMV row owned twice or out of range");
@@ -718,7 +718,7 @@ kie_status kie_validate_schedule(const kie_model_config* cfg, int32_t nwg, int32
   for (int k : kinds) {
     for (int w = 0; w < nwg; ++w) {
       int r0, r1;
-      kie::gemv_rows(m, k, nwg, w, &r0, &r1);
+      kie::gemv_rows_any(m, k, nwg, w, &r0, &r1);
       if (r1 - r0 > lp.rmax) return bad("GEMV rows of a workgroup exceed the LDS partial-sum rows");
       if (k == kie::PH_DOWN && 2 * (r1 - r0) > lp.desc - lp.own) return bad("down rows exceed the LDS row store");
     }

@@ -506,10 +506,15 @@ KIE_DI uint64_t matrix_offset(const KParams& p, int kind) {
 }
 
 // one wave's share of GEMV `kind` -> its 8-int descriptor (and the workgroup's rows)
+template <int G>
 KIE_DI void write_gemv_desc(const KParams& p, int kind, int nwg, int wg, int wave, int* dsc, int* wgrows) {
   const GemvShape sh = gemv_shape(p.m, kind);
   int r0, r1, c0, c1;
-  gemv_rows(p.m, kind, nwg, wg, &r0, &r1);
+  if constexpr (G > 2) {
+    gemv_rows_any(p.m, kind, nwg, wg, &r0, &r1);  // (mergers per query head)
+  } else {
+    gemv_rows(p.m, kind, nwg, wg, &r0, &r1);
+  }
   gemv_wave_chunks(r1 - r0, sh.K, wave, &c0, &c1);
   const int nb = col_blocks(sh.K);
   const uint64_t off = matrix_offset(p, kind) + packed_at((uint64_t)r0, 0, sh.K) + (uint64_t)c0 * kBlock;
@@ -528,6 +533,7 @@ KIE_DI void write_gemv_desc(const KParams& p, int kind, int nwg, int wg, int wav
 }
 
 // one wave's attention work at position pos -> 12-int descriptor
+template <int G>
 KIE_DI void write_attn_desc(const KParams& p, int nwg, int wg, int wave, int kpl, int pos, int* dsc) {
   const int n_ctx = pos + 1;
   AttnSeg seg[2];
@@ -555,6 +561,18 @@ KIE_DI void write_attn_desc(const KParams& p, int nwg, int wg, int wave, int kpl
     dsc[5 * s + 2] = kc;
     dsc[5 * s + 3] = nst;
     dsc[5 * s + 4] = hp;
+  }
+  if constexpr (G > 2) {
+    // one merger per query head (attn_mergers): the group's last G
+    // workgroups, workgroup w1 - 1 - h merging head h, coded as
+    // g + (h + 1) * 2^16 (a lone merger of every head stays g)
+    if (attn_mergers(p.m, nwg) > 1) {
+      const int g = attn_head(p.m.Hkv, nwg, wg);
+      int w0, w1;
+      split(nwg, p.m.Hkv, g, &w0, &w1);
+      const int h = w1 - 1 - wg;
+      merge_g = h < G ? g + ((h + 1) << 16) : -1;
+    }
   }
   dsc[10] = nseg;
   dsc[11] = merge_g;
@@ -1009,9 +1027,10 @@ KIE_DI void attn_pairs_full(const Dev& D, Cursor& cur, int& slot, Owed& owed, in
 // the record buffer.  A missing record reads as empty (m = -inf); on abort
 // or time-out the loop stops (the caller checks after its barrier).
 template <int K>
-KIE_DI void merger_poll_wide(const Dev& D, int l, int w_first, int nrec, int rw, int hd, const float* mlw,
-                             float* recs, uint32_t epoch) {
-  const int n = nrec * rw;
+KIE_DI void merger_poll_wide(const Dev& D, int l, int w_first, int nrec, int rw, int wpr, int hoff, int hd,
+                             const float* mlw, float* recs, uint32_t epoch) {
+  // words [hoff, hoff + wpr) of each record (of rw words) go to recs[r * wpr ...]
+  const int n = nrec * wpr;
   for (int base = D.tid; base < n; base += kThreads * K) {
     uint32_t off[K];
     uint32_t mask = 0;
@@ -1020,10 +1039,10 @@ KIE_DI void merger_poll_wide(const Dev& D, int l, int w_first, int nrec, int rw,
       const int i = base + k * kThreads;
       off[k] = 0;
       if (i < n) {
-        const int r = i / rw, o = i % rw;
+        const int r = i / wpr, o = i % wpr;
         const int si = (int)mlw[r * 8 + 7];
         if (si >= 0) {
-          off[k] = (uint32_t)((((uint64_t)l * D.nwg + w_first + r) * 2 + si) * rw + o);
+          off[k] = (uint32_t)((((uint64_t)l * D.nwg + w_first + r) * 2 + si) * rw + hoff + o);
           mask |= 1u << k;
         }
       }
@@ -1062,7 +1081,7 @@ KIE_DI void merger_poll_wide(const Dev& D, int l, int w_first, int nrec, int rw,
         float v = 0.f;
         if (mask & (1u << k)) {
           v = ll_f(vv[k]);
-        } else if ((i % rw) % (hd + 2) == 0) {
+        } else if ((i % wpr) % (hd + 2) == 0) {
           v = -INFINITY;  // missing record: empty
         }
         recs[i] = v;
@@ -1358,7 +1377,7 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
     const int kinds[5] = {PH_QKV, PH_O, PH_GU, PH_DOWN, PH_LM};
 #pragma unroll
     for (int k = 0; k < 5; ++k) {
-      write_gemv_desc(p, kinds[k], D.nwg, D.wg, D.wave, dsc, rows);
+      write_gemv_desc<G>(p, kinds[k], D.nwg, D.wg, D.wave, dsc, rows);
       if (D.lane == 0) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) D.desc[D.wave * kWaveDesc + 8 * k + i] = dsc[i];
@@ -1395,7 +1414,7 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
     int* adesc = D.desc + D.wave * kWaveDesc + kConsumerAttn;
     {
       int ad[12];
-      write_attn_desc(p, D.nwg, D.wg, D.wave, D.kpl, pos, ad);
+      write_attn_desc<G>(p, D.nwg, D.wg, D.wave, D.kpl, pos, ad);
 #pragma unroll
       for (int i = 0; i < 12; ++i) adesc[i] = ad[i];
     }
@@ -1604,7 +1623,50 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
         // merger: the workgroup holding head g's last key combines the
         // records of every workgroup that met head g
         const int merge_g = rfl(adesc[11]);
-        if (merge_g >= 0) {
+        bool lone_merger = merge_g >= 0;
+        if constexpr (G > 2) {
+          // a merger of one query head (attn_mergers): head mh's words of
+          // every record of the group, one weight per record, hd outputs
+          lone_merger = merge_g >= 0 && (merge_g >> 16) == 0;
+          if (merge_g >= 0 && (merge_g >> 16) > 0) {
+            const int g = merge_g & 0xFFFF, mh = (merge_g >> 16) - 1;
+            const int n_ctx = pos + 1;
+            const int w_first = attn_owner(Hkv, n_ctx, D.nwg, g, 0);
+            const int nrec = attn_owner(Hkv, n_ctx, D.nwg, g, n_ctx - 1) - w_first + 1;
+            for (int r = D.tid; r < nrec; r += kThreads) {
+              AttnSeg sgs[2];
+              sgs[0] = AttnSeg{0, 0, 0};
+              sgs[1] = AttnSeg{0, 0, 0};
+              const int ns = attn_segments(Hkv, n_ctx, D.nwg, w_first + r, sgs);
+              mlw[r * 8 + 7] = ns > 0 ? (float)((sgs[0].g == g) ? 0 : 1) : -1.f;
+            }
+            wg_sync();
+            float* recs = wrec;  // the wave records are consumed already
+            const int hw = hd + 2;
+            merger_poll_wide<9>(D, l, w_first, nrec, G * hw, hw, mh * hw, hd, mlw, recs, epoch);
+            wg_sync();
+            if (aborted(D)) { __builtin_amdgcn_s_waitcnt(kWaitAllVm); return; }
+            if (D.wave == 0) {
+              float M = -INFINITY;
+              for (int r = D.lane; r < nrec; r += kWave) M = fmaxf(M, recs[r * hw]);
+              M = wave_max(M);
+              float Ls = 0.f;
+              for (int r = D.lane; r < nrec; r += kWave)
+                Ls += (recs[r * hw] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(recs[r * hw] - M)) * recs[r * hw + 1];
+              Ls = wave_sum(Ls);
+              for (int r = D.lane; r < nrec; r += kWave)
+                mlw[r * 8] = (recs[r * hw] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(recs[r * hw] - M)) / Ls;
+            }
+            wg_sync();
+            for (int t = D.tid; t < hd; t += kThreads) {
+              float o = 0.f;
+#pragma unroll 4
+              for (int r = 0; r < nrec; ++r) o += mlw[r * 8] * recs[r * hw + 2 + t];
+              ll_storef(D.OB + (uint64_t)l * qd + (uint64_t)(g * G + mh) * hd + t, o, epoch);
+            }
+          }
+        }
+        if (lone_merger) {
           const int g = merge_g;
           const int n_ctx = pos + 1;
           const int w_first = attn_owner(Hkv, n_ctx, D.nwg, g, 0);
@@ -1623,7 +1685,7 @@ __global__ void __launch_bounds__(kThreads, 1) kie_monokernel(const KParams P) {
           float* recs = wrec;  // the wave records are consumed already
           const int rw = G * (hd + 2);
           if constexpr (G > 2) {
-            merger_poll_wide<17>(D, l, w_first, nrec, rw, hd, mlw, recs, epoch);
+            merger_poll_wide<17>(D, l, w_first, nrec, rw, rw, 0, hd, mlw, recs, epoch);
           } else {
           for (int base = D.tid; base < nrec * rw; base += kThreads * 8) {
             u64 vv[8];

@@ -270,6 +270,44 @@ KIE_HD void gemv_rows(const Dims& m, int kind, int nwg, int wg, int* r0, int* r1
   *r1 = b * s.unit_rows;
 }
 
+// Attention mergers per KV head group.  With more than two query heads per
+// KV head each query head has a merger of its own, the last G workgroups of
+// the group (workgroup w1 - 1 - h merges head h), when every group has that
+// many: one merger would read G heads of every record in the group, and a
+// workgroup's record poll is bound by its own memory requests.  Otherwise
+// the group's last workgroup merges all of its heads.
+KIE_HD int attn_mergers(const Dims& m, int nwg) { return (m.G > 2 && nwg / m.Hkv >= m.G) ? m.G : 1; }
+// gemv_rows with nm mergers per group left out of the O (and, in the
+// parallel block, the down) projection
+KIE_HD void gemv_rows_nm(const Dims& m, int kind, int nwg, int wg, int nm, int* r0, int* r1) {
+  GemvShape s = gemv_shape(m, kind);
+  int a, b;
+  if ((kind == PH_O || (m.parallel && kind == PH_DOWN)) && nwg > m.Hkv * nm) {
+    const int g = split_owner(wg, nwg, m.Hkv);
+    int w0, w1;
+    split(nwg, m.Hkv, g, &w0, &w1);
+    // index among the non-mergers (nm per earlier group); a merger gets the
+    // empty range where the next non-merger starts
+    const int first = w1 - nm;
+    split(s.rows / s.unit_rows, nwg - m.Hkv * nm, (wg < first ? wg : first) - g * nm, &a, &b);
+    if (wg >= first) b = a;
+  } else {
+    split(s.rows / s.unit_rows, nwg, wg, &a, &b);
+  }
+  *r0 = a * s.unit_rows;
+  *r1 = b * s.unit_rows;
+}
+// the rows of any shape (host side, and the kernels with more than two
+// query heads per KV head)
+KIE_HD void gemv_rows_any(const Dims& m, int kind, int nwg, int wg, int* r0, int* r1) {
+  const int nm = attn_mergers(m, nwg);
+  if (nm > 1) {
+    gemv_rows_nm(m, kind, nwg, wg, nm, r0, r1);
+  } else {
+    gemv_rows(m, kind, nwg, wg, r0, r1);
+  }
+}
+
 // The workgroup's row pairs are one contiguous stretch of nrows / 2 *
 // col_blocks(K) chunks; wave w takes chunks [c0, c1).
 KIE_HD int gemv_chunks(int nrows, int K) { return nrows / 2 * col_blocks(K); }
@@ -376,7 +414,7 @@ KIE_HD LdsPlan lds_plan(const Dims& m, int nwg, int budget) {
     if (k == PH_ATTN) continue;
     for (int w = 0; w < nwg; ++w) {
       int r0, r1;
-      gemv_rows(m, k, nwg, w, &r0, &r1);
+      gemv_rows_any(m, k, nwg, w, &r0, &r1);
       rmax = imax(rmax, r1 - r0);
       if (k == PH_DOWN) dmax = imax(dmax, r1 - r0);
     }
