@@ -42,9 +42,10 @@ def kernel_source_hash() -> str:
 
 
 def measured_traffic(cfg_name: str, prompt: int, steps: int):
-    """HBM bytes per launch from the committed rocprofv3 --pmc summary, only
-    if it was taken on the kernel source as it is now, for the same run"""
-    p = os.path.join(ROOT, "profiles", f"traffic_{cfg_name}.json")
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary of the
+    same run (config, prompt, decode steps), only if it was taken on the
+    kernel source as it is now"""
+    p = os.path.join(ROOT, "profiles", f"traffic_{cfg_name}_P{prompt}_N{steps}.json")
     if not os.path.exists(p):
         return None
     try:

@@ -1,6 +1,20 @@
 /*
  * kie.h - C ABI of the MI355X batch-1 fp16 decode monokernel.
  *
+ * Pages cited (by title; the shorthand used below in brackets):
+ *   [Malay explainer] "Startup Perancis Ini Kata Perisian Sahaja Cukup untuk
+ *     Pecutkan LLM 30x Lebih Pantas pada GPU Sedia Ada": approach list
+ *     ("Monokernel", "Delayed Tensor Parallelism (DTP)", lane-structured
+ *     transformer bullets), results table "Laneformer 2B: Keputusan yang
+ *     Ditunjukkan";
+ *   [Vietnamese explainer] "Kog: 'Phần mềm hóa rồng' - Tăng tốc suy luận AI
+ *     gấp 30 lần mà không cần phần cứng mới": the same list and table;
+ *   [Czech explainer] "Startup Kog dosahuje 3 000 tokenů/s na běžných GPU –
+ *     software poráží custom čipy": section "Software versus křemík";
+ *   [Chinese feature] the lynxflow.co article on Kog's low-level GPU tuning
+ *     (its first heading: "一场围绕“现有GPU”的推理竞赛"), section
+ *     "需求变化迫使Kog“做大”" on memory capacity and bandwidth.
+ *
  * What is computed.  Single-request (batch 1) greedy decoding of a
  * decoder-only transformer with fp16 weights, run as ONE persistent GPU
  * kernel per call: prefill, every decode step, the LM head and the greedy
@@ -9,7 +23,7 @@
  * (explainer pages, "Monokernel" bullet of the approach list and the
  * results table: FP16, batch size 1, no quantization, no speculative
  * decoding, no pruning, tokens per second per request; Czech explainer,
- * "Software versus silicon" section: one persistent program running prefill,
+ * "Software versus křemík" section: one persistent program running prefill,
  * decode and LM-head sampling in one go, without per-launch overhead or grid
  * synchronisations).  The pages do not define the block; this library
  * implements the Llama-style pre-norm block (RMSNorm, rotate-half RoPE,
@@ -125,7 +139,7 @@ kie_status kie_bind_memory(kie_ctx* ctx, void* d_packed, void* d_kv, void* d_wor
  * weights stay fp16 exactly as given: the pages' results are for FP16
  * decoding with no quantization or pruning (Malay and Vietnamese explainers,
  * results table "Laneformer 2B"), and decoding at batch 1 is bound by reading
- * every weight from memory once per token (Chinese feature, on decode being
+ * every weight from memory once per token (Chinese feature, section "需求变化迫使Kog“做大”", on decode being
  * memory-bandwidth bound), so the layout only reorders them for 16-byte
  * coalesced loads (row pairs in 1-KB chunks; RoPE partners and gate/up rows
  * paired) and adds nothing.  src must hold every pointer of kie_weights
@@ -141,7 +155,7 @@ kie_status kie_load_weights(kie_ctx* ctx, const kie_weights* host_src, void* str
  * prompt runs through the same persistent decode kernel, one position per
  * step, with the LM head only at the last position: the pages' monokernel
  * covers prefill as well as decode and LM-head sampling in one persistent
- * program (Czech explainer, "Software versus silicon" section).  Long
+ * program (Czech explainer, "Software versus křemík" section).  Long
  * prompts are split into several launches (kie_set_launch_steps).
  * KIE_ERR_INVALID_ARG for an empty prompt, KIE_ERR_CAPACITY if
  * pos + n_prompt > max_ctx, KIE_ERR_STATE if memory or weights are missing;
@@ -157,7 +171,7 @@ kie_status kie_prefill_scratch_bytes(const kie_ctx* ctx, int32_t chunk_tokens, s
  * positions pos..pos+n_prompt-1, t1, the last position's logits, position
  * += n_prompt), computed as dense products on the matrix cores.  The pages'
  * monokernel runs prefill on the GPU (Czech explainer, "Software versus
- * silicon" section); batching the prompt reads every weight once per chunk
+ * křemík" section); batching the prompt reads every weight once per chunk
  * of tokens instead of once per token.  All prompt tokens but the last go
  * through batched GEMMs (fp32 activations, fp16 weights, fp32 accumulation;
  * on the fp16 matrix cores, each activation a entering as hi = fp16(a) and
@@ -198,7 +212,7 @@ kie_status kie_prefill_batched_noalloc(kie_ctx* ctx, const int32_t* d_prompt, in
  * kie_set_launch_steps steps: the pages' monokernel, one program for the
  * whole decode loop with no kernel launches between layers or tokens and no
  * grid synchronisations (Malay and Vietnamese explainers, "Monokernel"
- * bullet; Czech explainer, "Software versus silicon" section), emitting
+ * bullet; Czech explainer, "Software versus křemík" section), emitting
  * tokens of a single request at batch 1 (results table "Laneformer 2B").
  * Step k consumes d_forced_in[k] when that
  * pointer is not NULL (teacher forcing), else the previous step's argmax (the

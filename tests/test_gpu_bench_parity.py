@@ -6,7 +6,9 @@
   teacher-forced decode steps in one launch of the persistent kernel: the
   prefill's logits and t1, every decode step's logits and token, and the
   keys and values of every layer at sampled prompt positions, against the
-  oracle with an fp16 KV cache (full prefill and decode in fp64).
+  oracle with an fp16 KV cache (full prefill and decode in fp64).  The same
+  for the lane-structured cfg3 (delayed residual, the pipelined phase order)
+  as bench.py --config cfg3 runs it.
 * cfg4's shape with two layers over its whole 32768-token prompt, prefilled
   token by token (the decode kernel, 4 query heads per KV head) and batched
   (16 chunks of 2048): layer-0 and layer-1 keys and values at sampled
@@ -29,7 +31,7 @@ import time
 import numpy as np
 import pytest
 
-from decode_persistent_monokernel_amd.config import CFG0, CFG2, CFG4
+from decode_persistent_monokernel_amd.config import CFG0, CFG2, CFG3, CFG4
 from decode_persistent_monokernel_amd.inputs import gen_weights, gen_prompt
 from oracle import Oracle
 from paritylib import REL_TOL, MARGIN, say, rel_l2, margin, compare_step, teacher_forced, layer1_kv_reference
@@ -63,17 +65,17 @@ def check_decode(name, ref, lg0, t1, toks, lgs):
     assert bad == 0
 
 
-def test_cfg2_bench_configuration_against_oracle():
-    cfg = CFG2
+@pytest.mark.parametrize("cfg,chunks", [(CFG2, (2048, 1024)), (CFG3, (2048,))], ids=["cfg2", "cfg3"])
+def test_bench_configuration_against_oracle(cfg, chunks):
     P, N = cfg.prompt_len, 16
-    say(f"case cfg2 bench configuration: L{cfg.n_layers} P={P} batched prefill, {N} teacher-forced steps")
+    say(f"case {cfg.name} bench configuration: L{cfg.n_layers} P={P} batched prefill, {N} teacher-forced steps")
     w = gen_weights(cfg)
     prompt = gen_prompt(cfg, n=P)
     t0 = time.time()
     ref = Oracle(cfg, w, kv_fp16=True).run(prompt, N)
     say(f"  oracle prefill + {N} steps: {time.time() - t0:.1f}s")
     pos = np.unique(np.concatenate([np.arange(0, 4), np.arange(4, P, 211), [P - 2, P - 1]]))
-    for chunk in (2048, 1024):
+    for chunk in chunks:
         say(f"  engine with prefill chunks of {chunk}")
         eng = make_engine(cfg, P + 512)
         eng.set_launch_steps(512)
@@ -88,7 +90,7 @@ def test_cfg2_bench_configuration_against_oracle():
         say(f"  KV cache of all {cfg.n_layers} layers at {len(pos)} positions: worst rel-L2 {worst_kv:.3e}")
         assert worst_kv <= REL_TOL
         toks, lgs = eng.decode(N, forced=ref["inputs"], want_logits=True)
-        check_decode(f"cfg2 chunk {chunk}", ref, lg0, t1, toks, lgs)
+        check_decode(f"{cfg.name} chunk {chunk}", ref, lg0, t1, toks, lgs)
         eng.close()
 
 
