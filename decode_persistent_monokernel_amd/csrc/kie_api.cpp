@@ -602,6 +602,51 @@ kie_status kie_phase_order(const kie_model_config* cfg, int32_t nwg, int32_t* ki
   return KIE_OK;
 }
 
+// packed row r of the fused QKV matrix (all q rows, then all k rows, then
+// all v rows; qkv_source_row) -> which = 0 q, 1 k, 2 v and head (the query
+// head for q, the KV head for k and v)
+static void qkv_row_head(const kie::Dims& m, int r, int* which, int* head) {
+  const int qd = m.H * m.hd, kvd = m.Hkv * m.hd;
+  *which = r < qd ? 0 : r < qd + kvd ? 1 : 2;
+  *head = (r - (*which == 0 ? 0 : *which == 1 ? qd : qd + kvd)) / m.hd;
+}
+
+kie_status kie_lane_placement(const kie_model_config* cfg, int32_t nwg, int32_t* lane_lo, int32_t* lane_hi) {
+  if (!cfg || nwg <= 0 || !lane_lo || !lane_hi || !check_config(*cfg).empty()) return KIE_ERR_INVALID_ARG;
+  const kie::Dims m = make_dims(*cfg);
+  if (!check_supported(m, nwg).empty()) return KIE_ERR_UNSUPPORTED;
+  const int qpl = m.H / cfg->n_lanes, fpl = m.F / cfg->n_lanes;  // query heads, FFN columns per lane
+  for (int w = 0; w < nwg; ++w) {
+    int lo[3] = {-1, -1, -1}, hi[3] = {-1, -1, -1};
+    // lanes of the query heads [h0, h1] (kind k)
+    auto take = [&](int k, int h0, int h1) {
+      lo[k] = lo[k] < 0 ? h0 / qpl : std::min(lo[k], h0 / qpl);
+      hi[k] = std::max(hi[k], h1 / qpl);
+    };
+    int r0, r1;
+    kie::gemv_rows_any(m, kie::PH_QKV, nwg, w, &r0, &r1);
+    for (int r = r0; r < r1; ++r) {
+      int which, head;
+      qkv_row_head(m, r, &which, &head);
+      if (which == 0) take(0, head, head);
+      else take(0, head * m.G, head * m.G + m.G - 1);
+    }
+    kie::AttnSeg seg[2];
+    const int ns = kie::attn_segments(m.Hkv, m.max_ctx, nwg, w, seg);
+    for (int i = 0; i < ns; ++i) take(1, seg[i].g * m.G, seg[i].g * m.G + m.G - 1);
+    kie::gemv_rows_any(m, kie::PH_GU, nwg, w, &r0, &r1);
+    if (r1 > r0) {  // packed gate/up row pair f is FFN column f
+      lo[2] = (r0 / 2) / fpl;
+      hi[2] = ((r1 - 1) / 2) / fpl;
+    }
+    for (int k = 0; k < 3; ++k) {
+      lane_lo[k * nwg + w] = lo[k];
+      lane_hi[k * nwg + w] = hi[k];
+    }
+  }
+  return KIE_OK;
+}
+
 kie_status kie_ring_depth(const kie_model_config* cfg, int32_t nwg, int32_t* depth) {
   if (!cfg || nwg <= 0 || !depth || !check_config(*cfg).empty()) return KIE_ERR_INVALID_ARG;
   const kie::Dims m = make_dims(*cfg);

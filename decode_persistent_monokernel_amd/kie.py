@@ -205,6 +205,21 @@ def ring_depth(cfg: ModelConfig, n_workgroups: int) -> int:
     return d.value
 
 
+def lane_placement(cfg: ModelConfig, n_workgroups: int):
+    """(lo, hi): int32 arrays [3, n_workgroups] of the lowest and highest lane
+    of each workgroup's QKV rows (0), attention head (1) and gate/up rows (2),
+    -1 where it has none"""
+    f = lib().kie_lane_placement
+    f.argtypes = [C.POINTER(ModelConfigC), C.c_int32, C.POINTER(C.c_int32), C.POINTER(C.c_int32)]
+    f.restype = C.c_int
+    n = 3 * n_workgroups
+    lo = (C.c_int32 * n)()
+    hi = (C.c_int32 * n)()
+    _check(f(C.byref(config_c(cfg)), n_workgroups, lo, hi))
+    return (np.array(lo, dtype=np.int32).reshape(3, n_workgroups),
+            np.array(hi, dtype=np.int32).reshape(3, n_workgroups))
+
+
 def kernel_name(cfg: ModelConfig, n_workgroups: int) -> str:
     """the decode kernel's symbol as profilers print it"""
     g = cfg.n_heads // cfg.n_kv_heads

@@ -287,6 +287,26 @@ kie_status kie_set_trace(kie_ctx* ctx, void* d_trace, int32_t steps);
 kie_status kie_phase_order(const kie_model_config* cfg, int32_t n_workgroups, int32_t* kind, int32_t* layer,
                            int32_t n);
 
+/* CPU-only: which lanes each workgroup's work belongs to.  Lane j owns the
+ * query heads [j*H/n_lanes, (j+1)*H/n_lanes) (a KV head belongs to the lanes
+ * of its query heads) and the FFN columns [j*F/n_lanes, (j+1)*F/n_lanes).
+ * For kind k = 0 (QKV rows), 1 (attention: the workgroup's KV head), 2
+ * (gate/up rows), lane_lo[k*n + w] .. lane_hi[k*n + w] are the lowest and
+ * highest lane of workgroup w's work (-1 where it has none of that kind),
+ * n = n_workgroups.  The kernel numbers its workgroups XCD by XCD
+ * (workgroup w runs on XCD w / (n / 8)), so for a lane-structured model
+ * whose lanes each fall on one block of n / n_lanes workgroups, each lane's
+ * attention heads and FFN columns run on one XCD: the Laneformer lanes of
+ * the pages (Malay and Vietnamese explainers, approach list,
+ * lane-structured transformer and Delayed Tensor Parallelism bullets) on the
+ * chip's XCDs.  The QKV rows are packed all q, then all k, then all v, so a
+ * workgroup's QKV rows belong to other lanes; the O and down projections are
+ * split by output rows over every workgroup and read every lane's output.
+ * KIE_ERR_INVALID_ARG for bad arguments, KIE_ERR_UNSUPPORTED for a shape the
+ * kernel does not run. */
+kie_status kie_lane_placement(const kie_model_config* cfg, int32_t n_workgroups, int32_t* lane_lo,
+                              int32_t* lane_hi);
+
 /* CPU-only: ring slots per wave (*depth, 8 or 10) of the decode kernel build
  * that a context for `cfg` on n_workgroups workgroups launches.  Each wave
  * streams its weight chunks through a ring of one-KB LDS slots (the weights

@@ -171,7 +171,8 @@ def _offsets(cfg):
     CFG0.with_(n_layers=2, vocab=512),
     CFG0.with_(n_layers=1, n_heads=8, n_kv_heads=2, head_dim=32, vocab=300, name="gqa"),
     CFG3.with_(n_layers=1, d_model=320, n_heads=4, n_kv_heads=4, head_dim=80, ffn_dim=864, vocab=100, n_lanes=4),
-], ids=["mha", "gqa", "hd80"])
+    CFG3.with_(n_layers=1, d_model=256, n_heads=4, n_kv_heads=2, head_dim=64, ffn_dim=512, vocab=100, n_lanes=2),
+], ids=["mha", "gqa", "hd80", "lanes-gqa"])
 def test_packer_is_a_permutation(cfg):
     w = gen_weights(cfg, std=0.5, threads=2)
     # distinct, recognisable norms
@@ -272,6 +273,35 @@ def test_ring_depth():
     assert kie.lib().kie_ring_depth(C.byref(kie.config_c(CFG2)), 256, None) == -1  # KIE_ERR_INVALID_ARG
     assert kie.lib().kie_ring_depth(None, 256, C.byref(d)) == -1  # KIE_ERR_INVALID_ARG
     assert kie.lib().kie_ring_depth(C.byref(kie.config_c(CFG2)), 0, C.byref(d)) == -1  # KIE_ERR_INVALID_ARG
+
+
+@needs_lib
+def test_lane_placement_maps_lanes_to_xcds():
+    """The lane-structured 2.4B shape (8 lanes of 4 heads and 864 FFN columns)
+    on 256 workgroups: workgroup w runs on XCD w // 32 (the kernel numbers its
+    workgroups XCD by XCD), and every workgroup's attention head and gate/up
+    rows belong to lane w // 32 alone, so lane j's attention and gate/up run
+    on XCD j.  The QKV rows (all q, then all k, then all v) do not follow the
+    lanes: the first three XCDs' workgroups compute the q rows of every lane."""
+    lo, hi = kie.lane_placement(CFG3, 256)
+    want = np.repeat(np.arange(8, dtype=np.int32), 32)
+    for k, name in ((1, "attention"), (2, "gate/up")):
+        assert np.array_equal(lo[k], want) and np.array_equal(hi[k], want), name
+    # q rows: 2560 of the 7680 rows, 30 rows per workgroup; lane j's 320 q rows
+    # on workgroups 320j/30 .. (320j + 319)/30
+    rows = 30 * np.arange(256)
+    assert np.array_equal(lo[0][:85], rows[:85] // 320)
+    assert (lo[0][86:171] >= 0).all() and not np.array_equal(lo[0], want)
+    # a lane block with two query heads per KV head and four lanes
+    g2 = CFG3.with_(n_layers=2, n_kv_heads=16, n_lanes=4)
+    lo, hi = kie.lane_placement(g2, 256)
+    want4 = np.repeat(np.arange(4, dtype=np.int32), 64)
+    for k in (1, 2):
+        assert np.array_equal(lo[k], want4) and np.array_equal(hi[k], want4), k
+    n = 3 * 256
+    a = (C.c_int32 * n)()
+    assert kie.lib().kie_lane_placement(C.byref(kie.config_c(CFG3)), 256, None, a) == -1  # KIE_ERR_INVALID_ARG
+    assert kie.lib().kie_lane_placement(None, 256, a, a) == -1
 
 
 @needs_lib
