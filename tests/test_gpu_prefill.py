@@ -106,6 +106,30 @@ def test_bad_token_in_batched_part_is_reported():
     eng.close()
 
 
+def test_activation_beyond_fp16_range_is_reported():
+    """RMSNorm gains of 30000 push the largest normalised activations (about
+    three times the RMS) past 65504, which the batched prefill's fp16 split cannot
+    carry: it latches KIE_ERR_RANGE instead of writing non-finite keys and
+    values.  The token-by-token path keeps fp32 activations and stays
+    finite on the same weights."""
+    cfg = CFG0.with_(seed_index=35, prompt_len=10, decode_steps=1)
+    say("case batched prefill with activations beyond the fp16 range")
+    w = gen_weights(cfg)
+    w["layers.0.attn_norm"] = np.full(cfg.d_model, 30000.0, dtype=np.float16)
+    prompt = gen_prompt(cfg)
+    eng = make_engine(cfg, 16)
+    eng.load_weights(w)
+    with pytest.raises(KieError) as ei:
+        eng.prefill_batched(prompt, chunk=4)
+    assert ei.value.status == -8  # KIE_ERR_RANGE
+    eng.close()
+    eng = make_engine(cfg, 16)
+    eng.load_weights(w)
+    _, lg = eng.prefill(prompt, want_logits=True)
+    assert np.isfinite(lg).all()
+    eng.close()
+
+
 def test_cfg2_batched_equals_token_by_token_prefill():
     cfg = CFG2
     P = cfg.prompt_len
