@@ -23,9 +23,12 @@
 
 Bar: relative L2 of the logits <= 1e-3 per step and the same token wherever
 the oracle's top-1/top-2 margin exceeds 1e-2; cache rows within one binary16
-ulp of the exact value (layer 0; layer 1 with 3e-4 of the rows' RMS for the
-fp32 error it inherits from layer 0) or relative L2 <= 1e-3 per layer.
+ulp of the exact value (layer 0; layer 1 with twice the spread that
+fp32-level rounding of layer 0's cache causes in the oracle itself,
+tests/golden/layer1_sensitivity.json) or relative L2 <= 1e-3 per layer.
 Every test prints its case before touching the GPU."""
+import json
+import os
 import time
 
 import numpy as np
@@ -44,6 +47,14 @@ if not torch.cuda.is_available():  # pragma: no cover - CPU container
 
 from decode_persistent_monokernel_amd.kie import Engine  # noqa: E402
 from test_gpu_large import assert_kv_close, gpu_kv_rows, layer0_kv_reference  # noqa: E402
+
+
+# how far fp32-level rounding of layer 0's keys and values moves layer 1 in
+# the oracle itself (written by oracle/layer1_sensitivity.py)
+with open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "layer1_sensitivity.json")) as _fh:
+    _SENS = json.load(_fh)
+L1_ELEM = _SENS["max_element_change_over_rms"]
+L1_POS = _SENS["max_position_rel_l2"]
 
 
 def make_engine(cfg, max_ctx):
@@ -100,7 +111,9 @@ def test_cfg4_layer1_kv_over_32k_prompt_both_prefills():
     say(f"case cfg4 2 layers, P={P}: layer-0/1 KV through both prefill paths")
     w = gen_weights(cfg)
     prompt = gen_prompt(cfg, n=P)
-    pos = np.unique(np.concatenate([np.arange(0, 3), np.arange(2047, P, 4093), [2048, 4096, P - 2, P - 1]]))
+    rng = np.random.default_rng(41)
+    pos = np.unique(np.concatenate([np.arange(0, 3), np.arange(2047, P, 4093), [2048, 4096, P - 2, P - 1],
+                                    rng.integers(0, P, 32)]))
     t0 = time.time()
     orc = Oracle(cfg, w, kv_fp16=True)
     k1, v1 = layer1_kv_reference(orc, prompt, pos)
@@ -120,19 +133,21 @@ def test_cfg4_layer1_kv_over_32k_prompt_both_prefills():
             toks[mode], logits[mode] = eng.prefill(prompt, want_logits=True)
         assert_kv_close(gpu_kv_rows(eng, cfg, 0, 0, pos), k0, f"{mode} layer-0 K")
         assert_kv_close(gpu_kv_rows(eng, cfg, 0, 1, pos), v0, f"{mode} layer-0 V")
-        # Layer 1 inherits the fp32 error of layer 0's attention over up to
-        # 32768 keys (whose fp16 keys and values can round to the other
-        # neighbour than the oracle's where the fp32 value sits near a
-        # rounding boundary), its O projection and its 14336-wide MLP.
-        # Measured before the final rounding: up to 6e-5 of the rows' RMS
-        # token by token, 2e-4 batched (matrix cores).  Allowed: one ulp plus
-        # 3e-4 of the RMS per element, and 5e-4 relative L2 per layer (the
-        # fp16 rounding alone is ~2e-4); the logits bar is 1e-3.
+        # Layer 1 inherits layer 0's cache: K and V computed in fp32 (error
+        # ~4e-6 relative) round to the other binary16 neighbour than the
+        # fp64 oracle's for ~0.5 % of the entries, and some positions (a few
+        # keys dominating the softmax) amplify those one-ulp differences.
+        # The oracle itself, its layer-0 K and V perturbed by that much
+        # before the rounding, moves layer 1 by up to L1_ELEM of the rows'
+        # RMS per element and L1_POS relative L2 per position
+        # (tests/golden/layer1_sensitivity.json).  Allowed: one ulp plus
+        # twice L1_ELEM per element; relative L2 over the sampled rows at
+        # the 1e-3 bar, about twice L1_POS.
         g1k, g1v = gpu_kv_rows(eng, cfg, 1, 0, pos), gpu_kv_rows(eng, cfg, 1, 1, pos)
-        assert_kv_close(g1k, k1, f"{mode} layer-1 K", pre_round=3e-4)
-        assert_kv_close(g1v, v1, f"{mode} layer-1 V", pre_round=3e-4)
+        assert_kv_close(g1k, k1, f"{mode} layer-1 K", pre_round=2 * L1_ELEM)
+        assert_kv_close(g1v, v1, f"{mode} layer-1 V", pre_round=2 * L1_ELEM)
         say(f"  {mode} layer-1 rel-L2 K {rel_l2(g1k, k1):.2e} V {rel_l2(g1v, v1):.2e}")
-        assert rel_l2(g1k, k1) <= 5e-4 and rel_l2(g1v, v1) <= 5e-4
+        assert rel_l2(g1k, k1) <= REL_TOL and rel_l2(g1v, v1) <= REL_TOL
         eng.close()
     r = rel_l2(logits["batched"], logits["tokens"])
     say(f"  last-position logits, batched vs token by token: rel-L2 {r:.3e}; t1 {toks['batched']}/{toks['tokens']}")

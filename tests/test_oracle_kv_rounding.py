@@ -35,3 +35,21 @@ def test_fp16_cache_rounding_exceeds_the_bar_at_full_size():
     assert min(c[("cfg2", 28)]["rel_l2_per_step"]) > 1e-3
     assert 2e-4 < c[("cfg2", 1)]["max"] < 1e-3    # one layer: within it
     assert 2e-4 < c[("cfg1", 24)]["max"] < 1e-3
+
+
+def test_recorded_layer1_sensitivity_is_consistent():
+    """tests/golden/layer1_sensitivity.json (oracle/layer1_sensitivity.py):
+    relative noise of 4e-6 (an fp32 dot product over 4096 terms) on the 8B
+    shape's layer-0 K and V makes a few per thousand of the cached entries
+    round to the other binary16 neighbour (an fp16 ulp is about 1e-3
+    relative); layer 1 then moves by more than the 3e-4 of the RMS that an
+    element-wise bound drawn from a handful of positions would allow, and by
+    less than the 1e-3 relative-L2 bar at every position."""
+    with open(os.path.join(ROOT, "tests", "golden", "layer1_sensitivity.json")) as fh:
+        s = json.load(fh)
+    assert s["config"] == "cfg4" and s["layers"] == 2 and s["sigma"] == 4e-6 and len(s["runs"]) >= 3
+    for r in s["runs"]:
+        assert 1e-3 < r["flip_fraction"] < 1e-2, r
+        assert r["median_position_rel_l2"] < r["max_position_rel_l2"] < 1e-3, r
+    assert 3e-4 < s["max_element_change_over_rms"] < 1e-2
+    assert s["max_element_change_over_rms"] == max(r["max_element_change_over_rms"] for r in s["runs"])
