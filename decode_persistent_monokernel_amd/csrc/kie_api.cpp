@@ -631,9 +631,8 @@ kie_status kie_lane_placement(const kie_model_config* cfg, int32_t nwg, int32_t*
       if (which == 0) take(0, head, head);
       else take(0, head * m.G, head * m.G + m.G - 1);
     }
-    kie::AttnSeg seg[2];
-    const int ns = kie::attn_segments(m.Hkv, m.max_ctx, nwg, w, seg);
-    for (int i = 0; i < ns; ++i) take(1, seg[i].g * m.G, seg[i].g * m.G + m.G - 1);
+    const int g = kie::attn_head(m.Hkv, nwg, w);  // the workgroup's KV head (attention group)
+    take(1, g * m.G, g * m.G + m.G - 1);
     kie::gemv_rows_any(m, kie::PH_GU, nwg, w, &r0, &r1);
     if (r1 > r0) {  // packed gate/up row pair f is FFN column f
       lo[2] = (r0 / 2) / fpl;
