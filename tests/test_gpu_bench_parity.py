@@ -9,6 +9,9 @@
   oracle with an fp16 KV cache (full prefill and decode in fp64).  The same
   for the lane-structured cfg3 (delayed residual, the pipelined phase order)
   as bench.py --config cfg3 runs it.
+* the benchmark's own cfg2 launch: 512 free-running greedy steps (no
+  teacher forcing) after the batched prefill, every step checked with the
+  oracle fed the GPU's token stream.
 * cfg4's shape with two layers over its whole 32768-token prompt, prefilled
   token by token (the decode kernel, 4 query heads per KV head) and batched
   (16 chunks of 2048): layer-0 and layer-1 keys and values at sampled
@@ -103,6 +106,32 @@ def test_bench_configuration_against_oracle(cfg, chunks):
         toks, lgs = eng.decode(N, forced=ref["inputs"], want_logits=True)
         check_decode(f"{cfg.name} chunk {chunk}", ref, lg0, t1, toks, lgs)
         eng.close()
+
+
+def test_cfg2_bench_launch_free_running_against_oracle():
+    """The benchmark's own run: cfg2, the 2048-token prompt through the
+    batched prefill, then one launch of 512 greedy decode steps that feed
+    back their own tokens (no teacher forcing), with logits.  The oracle is
+    fed the GPU's token stream (t1, then each emitted token) and must agree
+    on every step's logits and, where its margin allows, token (the fp64
+    oracle takes ~0.15 s a step, ~100 s for the launch)."""
+    cfg = CFG2
+    P, N = cfg.prompt_len, 512
+    say(f"case cfg2 benchmark launch: P={P}, {N} free-running steps in one launch")
+    w = gen_weights(cfg)
+    prompt = gen_prompt(cfg, n=P)
+    eng = make_engine(cfg, P + N + 1)
+    eng.set_launch_steps(N)
+    eng.load_weights(w)
+    t1, lg0 = eng.prefill_batched(prompt, want_logits=True)
+    toks, lgs = eng.decode(N, want_logits=True)
+    eng.close()
+    assert np.isfinite(lgs).all()
+    fed = [t1] + [int(t) for t in toks[: N - 1]]
+    t0 = time.time()
+    ref = Oracle(cfg, w, kv_fp16=True).run(prompt, N, forced=fed)
+    say(f"  oracle prefill + {N} steps fed with the GPU's tokens: {time.time() - t0:.1f}s")
+    check_decode("cfg2 benchmark launch", ref, lg0, t1, toks, lgs)
 
 
 def test_cfg4_layer1_kv_over_32k_prompt_both_prefills():
