@@ -9,7 +9,7 @@
   oracle with an fp16 KV cache (full prefill and decode in fp64).  The same
   for the lane-structured cfg3 (delayed residual, the pipelined phase order)
   as bench.py --config cfg3 runs it.
-* the benchmark's own cfg2 launch: 512 free-running greedy steps (no
+* the benchmark's own cfg2 and cfg3 launches: 512 free-running greedy steps (no
   teacher forcing) after the batched prefill, every step checked with the
   oracle fed the GPU's token stream.
 * cfg4's shape with two layers over its whole 32768-token prompt, prefilled
@@ -108,16 +108,17 @@ def test_bench_configuration_against_oracle(cfg, chunks):
         eng.close()
 
 
-def test_cfg2_bench_launch_free_running_against_oracle():
-    """The benchmark's own run: cfg2, the 2048-token prompt through the
+@pytest.mark.parametrize("cfg", [CFG2, CFG3], ids=["cfg2", "cfg3"])
+def test_bench_launch_free_running_against_oracle(cfg):
+    """The benchmark's own run of cfg2 (and of the lane-structured cfg3, as
+    bench.py --config cfg3 runs it): the 2048-token prompt through the
     batched prefill, then one launch of 512 greedy decode steps that feed
     back their own tokens (no teacher forcing), with logits.  The oracle is
     fed the GPU's token stream (t1, then each emitted token) and must agree
     on every step's logits and, where its margin allows, token (the fp64
     oracle takes ~0.15 s a step, ~100 s for the launch)."""
-    cfg = CFG2
     P, N = cfg.prompt_len, 512
-    say(f"case cfg2 benchmark launch: P={P}, {N} free-running steps in one launch")
+    say(f"case {cfg.name} benchmark launch: P={P}, {N} free-running steps in one launch")
     w = gen_weights(cfg)
     prompt = gen_prompt(cfg, n=P)
     eng = make_engine(cfg, P + N + 1)
@@ -131,7 +132,7 @@ def test_cfg2_bench_launch_free_running_against_oracle():
     t0 = time.time()
     ref = Oracle(cfg, w, kv_fp16=True).run(prompt, N, forced=fed)
     say(f"  oracle prefill + {N} steps fed with the GPU's tokens: {time.time() - t0:.1f}s")
-    check_decode("cfg2 benchmark launch", ref, lg0, t1, toks, lgs)
+    check_decode(f"{cfg.name} benchmark launch", ref, lg0, t1, toks, lgs)
 
 
 def test_cfg4_layer1_kv_over_32k_prompt_both_prefills():
